@@ -1,0 +1,67 @@
+"""Plants plausible mistakes in a temporary copy of the oracle and checks
+that the pins catch every one (CPU only; the real oracle is never edited)."""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = {
+    "eps_outside_root": ("np.sqrt(ms + eps)", "(np.sqrt(ms) + eps)"),
+    "gain_offset": ("return x / np.sqrt(ms + eps) * _f64(gain)",
+                    "return x / np.sqrt(ms + eps) * (1 + _f64(gain))"),
+    "rope_sin_sign": ("x[..., : rd // 2] = a * cos - b * sin",
+                      "x[..., : rd // 2] = a * cos + b * sin"),
+    "rope_freq_exponent": ("inv_freq = theta ** (-2.0 * i / rot_dim)",
+                           "inv_freq = theta ** (-1.0 * i / rot_dim)"),
+    "rope_position_off_by_one": ("positions = start_pos + np.arange(B)",
+                                 "positions = start_pos + 1 + np.arange(B)"),
+    "gqa_map_modulo": ("return h // (n_heads // n_kv_heads)", "return h % n_kv_heads"),
+    "causal_leaks_next_key": ("<= (start_pos + np.arange(B))", "<= (start_pos + 1 + np.arange(B))"),
+    "softcap_before_scale": (
+        "s = (q[:, h, :] @ k_all[:, g, :].T) * scale\n        if softcap:\n"
+        "            s = softcap * np.tanh(s / softcap)",
+        "s = (q[:, h, :] @ k_all[:, g, :].T)\n        if softcap:\n"
+        "            s = softcap * np.tanh(s / softcap)\n        s = s * scale"),
+    "gate_dropped": ("o = o * (1.0 / (1.0 + np.exp(-_f64(gate))))", "o = o"),
+    "gate_interleaved": ("q, gate = qg[:, : Hq * hd], None", "q, gate = qg[:, 0::2], None"),
+    "k_bias_dropped": ("q, k, v = q + _f64(w[\"bq\"]), k + _f64(w[\"bk\"]), v + _f64(w[\"bv\"])",
+                       "q, k, v = q + _f64(w[\"bq\"]), k, v + _f64(w[\"bv\"])"),
+    "qk_norm_dropped": ("        q = rms_norm(q, w[\"q_norm\"], spec.rms_eps)\n"
+                        "        k = rms_norm(k, w[\"k_norm\"], spec.rms_eps)\n",
+                        "        pass\n"),
+    "attn_residual_dropped": ("x1 = x + o.reshape(B, -1)", "x1 = 0 * x + o.reshape(B, -1)"),
+    "wo_transposed": ("x1 = x + o.reshape(B, -1) @ _f64(w[\"wo\"]).T",
+                      "x1 = x + o.reshape(B, -1) @ _f64(w[\"wo\"]).reshape("
+                      "_f64(w[\"wo\"]).shape[::-1])"),
+    "ffn_norm_reads_x": ("h2 = rms_norm(x1, w[\"g_ffn\"]", "h2 = rms_norm(x, w[\"g_ffn\"]"),
+    "silu_as_sigmoid": ("return z / (1.0 + np.exp(-z))", "return 1 / (1.0 + np.exp(-z))"),
+    "prefix_v_reads_k": ("v_all = np.concatenate([_f64(prefix_v)",
+                         "v_all = np.concatenate([_f64(prefix_k)"),
+    "decode_skips_new_row": ("k_all = np.concatenate([_f64(cache_k)[:rows], _f64(k)[None]])",
+                             "k_all = np.concatenate([_f64(cache_k)[:rows], "
+                             "_f64(cache_k)[rows - 1:rows]])"),
+}
+
+
+@pytest.fixture(scope="module")
+def oracle_source():
+    with open(os.path.join(ROOT, "oracle", "__init__.py")) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, oracle_source, tmp_path):
+    before, after = MUTANTS[name]
+    assert before in oracle_source, f"mutation site of {name} not found"
+    for d in ("oracle", "synth", "tests"):
+        shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
+                        ignore=shutil.ignore_patterns("__pycache__", "golden"))
+    (tmp_path / "oracle" / "__init__.py").write_text(oracle_source.replace(before, after))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        "tests/test_oracle_pins.py"], cwd=tmp_path, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode != 0, f"planted mistake {name} went unnoticed:\n{r.stdout[-2000:]}"

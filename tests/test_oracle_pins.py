@@ -1,0 +1,489 @@
+"""Pins of the CPU oracle to things other than itself: brute force on tiny
+inputs, closed forms, invariants the pages fix, and special cases that reduce
+to library routines.  CPU only."""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import synth
+
+RNG = np.random.default_rng(1234)
+
+
+class Spec:
+    """A small layer description with the fields the oracle reads."""
+
+    def __init__(self, **kw):
+        self.n_heads, self.n_kv_heads, self.head_dim = 4, 2, 8
+        self.d_model, self.d_ff = 32, 48
+        self.rms_eps, self.rope_theta, self.rope_layout = 1e-5, 1e4, "neox"
+        self.softcap, self.gated, self.qkv_bias, self.qk_norm = 0.0, False, False, False
+        self.__dict__.update(kw)
+
+
+def rand_layer(spec, scale=0.2, rng=RNG):
+    qw, kw = spec.n_heads * spec.head_dim, spec.n_kv_heads * spec.head_dim
+    d, f = spec.d_model, spec.d_ff
+    w = {
+        "g_attn": 1 + 0.1 * rng.standard_normal(d),
+        "wq": scale * rng.standard_normal(((2 if spec.gated else 1) * qw, d)),
+        "wk": scale * rng.standard_normal((kw, d)),
+        "wv": scale * rng.standard_normal((kw, d)),
+        "wo": scale * rng.standard_normal((d, qw)),
+        "g_ffn": 1 + 0.1 * rng.standard_normal(d),
+        "wg": scale * rng.standard_normal((f, d)),
+        "wu": scale * rng.standard_normal((f, d)),
+        "wd": scale * rng.standard_normal((d, f)),
+    }
+    if spec.qkv_bias:
+        w.update(bq=0.3 * rng.standard_normal(qw), bk=0.3 * rng.standard_normal(kw),
+                 bv=0.3 * rng.standard_normal(kw))
+    if spec.qk_norm:
+        w.update(q_norm=1 + 0.2 * rng.standard_normal(spec.head_dim),
+                 k_norm=1 + 0.2 * rng.standard_normal(spec.head_dim))
+    return w
+
+
+def rel(a, b):
+    return float(np.linalg.norm(np.asarray(a) - np.asarray(b)) / np.linalg.norm(b))
+
+
+# ---------------------------------------------------------------------------
+# brute-force attention: per token, per head, per key scalar loops in fp64
+
+
+def brute_attention(q, k_all, v_all, start_pos, softcap=0.0, gate=None):
+    B, Hq, hd = q.shape
+    Hkv = k_all.shape[1]
+    per_group = Hq // Hkv
+    out = np.zeros((B, Hq, hd))
+    for b in range(B):
+        last = start_pos + b
+        for h in range(Hq):
+            g = h // per_group
+            scores = []
+            for j in range(last + 1):
+                s = 0.0
+                for c in range(hd):
+                    s += float(q[b, h, c]) * float(k_all[j, g, c])
+                s = s / math.sqrt(hd)
+                if softcap:
+                    s = softcap * math.tanh(s / softcap)
+                scores.append(s)
+            m = max(scores)
+            e = [math.exp(s - m) for s in scores]
+            z = sum(e)
+            for c in range(hd):
+                acc = 0.0
+                for j in range(last + 1):
+                    acc += e[j] / z * float(v_all[j, g, c])
+                if gate is not None:
+                    acc *= 1.0 / (1.0 + math.exp(-float(gate[b, h, c])))
+                out[b, h, c] = acc
+    return out
+
+
+@pytest.mark.parametrize("B,S", [(2, 0), (3, 0), (4, 0), (2, 3), (4, 5)])
+@pytest.mark.parametrize("softcap", [0.0, 1.0])
+@pytest.mark.parametrize("gated", [False, True])
+def test_attention_matches_brute_force(B, S, softcap, gated):
+    Hq, Hkv, hd = 4, 2, 8
+    q = 2.0 * RNG.standard_normal((B, Hq, hd))
+    k_all = 2.0 * RNG.standard_normal((S + B, Hkv, hd))
+    v_all = RNG.standard_normal((S + B, Hkv, hd))
+    gate = RNG.standard_normal((B, Hq, hd)) if gated else None
+    got = oracle.causal_gqa_attention(q, k_all, v_all, S, softcap, gate)
+    want = brute_attention(q, k_all, v_all, S, softcap, gate)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_single_key_returns_its_value():
+    # token 0 with no prefix sees only itself: output is v of its KV head, exactly
+    Hq, Hkv, hd = 6, 3, 4
+    q = RNG.standard_normal((1, Hq, hd))
+    k = RNG.standard_normal((1, Hkv, hd))
+    v = RNG.standard_normal((1, Hkv, hd))
+    o = oracle.causal_gqa_attention(q, k, v, 0)
+    for h in range(Hq):
+        assert np.array_equal(o[0, h], v[0, h // 2])
+
+
+def test_attention_equal_keys_average_values():
+    B, S, Hq, Hkv, hd = 3, 4, 2, 1, 8
+    q = RNG.standard_normal((B, Hq, hd))
+    k_all = np.repeat(RNG.standard_normal((1, Hkv, hd)), S + B, axis=0)
+    v_all = RNG.standard_normal((S + B, Hkv, hd))
+    o = oracle.causal_gqa_attention(q, k_all, v_all, S)
+    for b in range(B):
+        want = v_all[: S + b + 1, 0].mean(axis=0)
+        for h in range(Hq):
+            np.testing.assert_allclose(o[b, h], want, rtol=1e-12, atol=1e-14)
+
+
+def test_gqa_head_map_one_hot():
+    # value of KV head g is the one-hot e_g, so head h must return e_{h // group}
+    B, S, Hq, Hkv, hd = 3, 2, 8, 4, 8
+    q = RNG.standard_normal((B, Hq, hd))
+    k_all = RNG.standard_normal((S + B, Hkv, hd))
+    v_all = np.zeros((S + B, Hkv, hd))
+    for g in range(Hkv):
+        v_all[:, g, g] = 1.0
+    o = oracle.causal_gqa_attention(q, k_all, v_all, S)
+    for h in range(Hq):
+        want = np.zeros(hd)
+        want[h // (Hq // Hkv)] = 1.0
+        np.testing.assert_allclose(o[:, h], np.broadcast_to(want, (B, hd)), atol=1e-14)
+    assert [oracle.kv_head_of(h, 24, 8) for h in range(24)] == [h // 3 for h in range(24)]
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    B, S, Hq, Hkv, hd = 4, 3, 6, 2, 8
+    q = RNG.standard_normal((B, Hq, hd))
+    k_all = RNG.standard_normal((S + B, Hkv, hd))
+    v_all = RNG.standard_normal((S + B, Hkv, hd))
+    gqa = oracle.causal_gqa_attention(q, k_all, v_all, S)
+    mha = oracle.causal_gqa_attention(q, np.repeat(k_all, Hq // Hkv, axis=1),
+                                      np.repeat(v_all, Hq // Hkv, axis=1), S)
+    np.testing.assert_allclose(gqa, mha, rtol=1e-13, atol=1e-14)
+
+
+def test_softcap_limits_and_gate_limits():
+    B, S, Hq, Hkv, hd = 3, 2, 4, 2, 8
+    q = 3 * RNG.standard_normal((B, Hq, hd))
+    k_all = 3 * RNG.standard_normal((S + B, Hkv, hd))
+    v_all = RNG.standard_normal((S + B, Hkv, hd))
+    plain = oracle.causal_gqa_attention(q, k_all, v_all, S)
+    np.testing.assert_allclose(oracle.causal_gqa_attention(q, k_all, v_all, S, 1e9), plain,
+                               rtol=1e-10)
+    assert rel(oracle.causal_gqa_attention(q, k_all, v_all, S, 0.5), plain) > 1e-3
+    big = np.full((B, Hq, hd), 60.0)
+    np.testing.assert_allclose(oracle.causal_gqa_attention(q, k_all, v_all, S, 0, big), plain,
+                               rtol=1e-12)
+    zero = np.zeros((B, Hq, hd))
+    np.testing.assert_allclose(oracle.causal_gqa_attention(q, k_all, v_all, S, 0, zero),
+                               plain / 2, rtol=1e-14)
+
+
+def test_softcap_squashes_each_score():
+    # with a cap c, a single huge score behaves like c: two keys with scores
+    # +inf-ish and 0 give weights e^c/(e^c+1) and 1/(e^c+1)
+    hd, c = 4, 2.0
+    q = np.zeros((2, 1, hd)); q[1, 0, 0] = 1e4
+    k = np.zeros((2, 1, hd)); k[0, 0, 0] = 1.0
+    v = np.zeros((2, 1, hd)); v[0, 0, 1] = 1.0; v[1, 0, 2] = 1.0
+    o = oracle.causal_gqa_attention(q, k, v, 0, softcap=c)
+    w0 = math.exp(c) / (math.exp(c) + 1.0)
+    np.testing.assert_allclose(o[1, 0], [0, w0, 1 - w0, 0], rtol=1e-12, atol=1e-15)
+
+
+def test_attention_matches_torch_sdpa():
+    B, Hq, Hkv, hd = 7, 6, 2, 16
+    q = RNG.standard_normal((B, Hq, hd))
+    k = RNG.standard_normal((B, Hkv, hd))
+    v = RNG.standard_normal((B, Hkv, hd))
+    got = oracle.causal_gqa_attention(q, k, v, 0)
+    t = lambda a: torch.from_numpy(a).permute(1, 0, 2)[None]
+    want = F.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=True, enable_gqa=True)
+    np.testing.assert_allclose(got, want[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm, SwiGLU
+
+
+def test_rms_norm_constant_row_closed_form():
+    c, eps = 0.37, 1e-5
+    g = 1 + 0.1 * RNG.standard_normal(16)
+    got = oracle.rms_norm(np.full((1, 16), c), g, eps)
+    np.testing.assert_allclose(got[0], g * c / math.sqrt(c * c + eps), rtol=1e-15)
+
+
+def test_rms_norm_scale_invariant_without_eps_and_matches_torch():
+    x = RNG.standard_normal((5, 32))
+    g = 1 + 0.1 * RNG.standard_normal(32)
+    np.testing.assert_allclose(oracle.rms_norm(7.5 * x, g, 0.0), oracle.rms_norm(x, g, 0.0),
+                               rtol=1e-13)
+    want = F.rms_norm(torch.from_numpy(x), (32,), torch.from_numpy(g), eps=1e-5).numpy()
+    np.testing.assert_allclose(oracle.rms_norm(x, g, 1e-5), want, rtol=1e-13)
+
+
+def test_swiglu_matches_torch():
+    h = RNG.standard_normal((3, 12))
+    wg, wu, wd = (RNG.standard_normal(s) for s in [(20, 12), (20, 12), (12, 20)])
+    th = torch.from_numpy(h)
+    want = (F.silu(th @ torch.from_numpy(wg).T) * (th @ torch.from_numpy(wu).T)) \
+        @ torch.from_numpy(wd).T
+    np.testing.assert_allclose(oracle.swiglu_ffn(h, wg, wu, wd), want.numpy(), rtol=1e-12)
+    np.testing.assert_allclose(oracle.silu(np.array([0.0, 1.0, -2.0])),
+                               [0.0, 1 / (1 + math.exp(-1)), -2 / (1 + math.exp(2))], rtol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# RoPE
+
+
+def test_rope_hand_example_neox_and_norm():
+    x = np.zeros((1, 1, 4)); x[0, 0, 0] = 1.0
+    neox = oracle.apply_rope(x, [1], 1e4, "neox")[0, 0]
+    norm = oracle.apply_rope(x, [1], 1e4, "norm")[0, 0]
+    np.testing.assert_allclose(neox, [math.cos(1), 0, math.sin(1), 0], atol=1e-16)
+    np.testing.assert_allclose(norm, [math.cos(1), math.sin(1), 0, 0], atol=1e-16)
+    # the second pair turns at theta^(-2/4) = 1/100 rad per position
+    x = np.zeros((1, 1, 4)); x[0, 0, 1] = 1.0
+    np.testing.assert_allclose(oracle.apply_rope(x, [3], 1e4, "neox")[0, 0],
+                               [0, math.cos(0.03), 0, math.sin(0.03)], atol=1e-16)
+
+
+def test_rope_position_zero_is_identity_and_pairs_keep_norm():
+    x = RNG.standard_normal((5, 3, 16))
+    assert np.array_equal(oracle.apply_rope(x[:1], [0], 5e5), x[:1])
+    y = oracle.apply_rope(x, np.arange(5) * 37, 5e5)
+    pair = lambda a: a[..., :8] ** 2 + a[..., 8:] ** 2
+    np.testing.assert_allclose(pair(y), pair(x), rtol=1e-13)
+
+
+def test_rope_matches_complex_rotation():
+    # neox pairs (i, i+hd/2) as the complex number x_i + 1j*x_{i+hd/2}
+    hd, pos = 16, np.array([0, 1, 7, 4095])
+    x = RNG.standard_normal((4, 2, hd))
+    z = x[..., : hd // 2] + 1j * x[..., hd // 2:]
+    freqs = np.array([5e5 ** (-2 * i / hd) for i in range(hd // 2)])
+    zr = z * np.exp(1j * pos[:, None, None] * freqs[None, None, :])
+    y = oracle.apply_rope(x, pos, 5e5, "neox")
+    np.testing.assert_allclose(y[..., : hd // 2], zr.real, atol=1e-12)
+    np.testing.assert_allclose(y[..., hd // 2:], zr.imag, atol=1e-12)
+
+
+def test_rope_relative_position_property():
+    hd = 32
+    q, k = RNG.standard_normal((1, 1, hd)), RNG.standard_normal((1, 1, hd))
+    def logit(pq, pk):
+        return float(np.sum(oracle.apply_rope(q, [pq], 1e4) * oracle.apply_rope(k, [pk], 1e4)))
+    for delta in (1, 100, 3000):
+        assert abs(logit(10 + delta, 3 + delta) - logit(10, 3)) < 1e-9
+
+
+def test_rope_options_freq_factors_partial_and_mscale():
+    hd, pos = 8, [5]
+    x = RNG.standard_normal((1, 1, hd))
+    # frequency factors of 2 halve every angle: position 5 turns like 2.5
+    half = oracle.apply_rope(x, pos, 1e4, freq_factors=np.full(4, 2.0))
+    np.testing.assert_allclose(half, oracle.apply_rope(x, [2.5], 1e4), atol=1e-14)
+    # a partial rotated width leaves the tail channels alone
+    part = oracle.apply_rope(x, pos, 1e4, rot_dim=4)
+    assert np.array_equal(part[..., 4:], x[..., 4:])
+    np.testing.assert_allclose(part[..., :4], oracle.apply_rope(x[..., :4], pos, 1e4), atol=1e-15)
+    # the attention factor scales the rotated channels only
+    ms = oracle.apply_rope(x, pos, 1e4, rot_dim=4, mscale=0.5)
+    np.testing.assert_allclose(ms[..., :4], 0.5 * part[..., :4], atol=1e-15)
+    assert np.array_equal(ms[..., 4:], x[..., 4:])
+
+
+# ---------------------------------------------------------------------------
+# projections, positions, the layer
+
+
+def test_projection_orientation_one_hot_input():
+    spec = Spec(rope_theta=None)
+    w = rand_layer(spec)
+    j = 5
+    h = np.zeros((1, spec.d_model)); h[0, j] = 1.0
+    q, gate, k, v = oracle.project_qkv(h, w, spec, [0])
+    np.testing.assert_array_equal(q.reshape(-1), w["wq"][:, j])
+    np.testing.assert_array_equal(k.reshape(-1), w["wk"][:, j])
+    np.testing.assert_array_equal(v.reshape(-1), w["wv"][:, j])
+    assert gate is None
+
+
+def test_gated_wq_split_first_half_q_second_half_gate():
+    spec = Spec(gated=True, rope_theta=None)
+    w = rand_layer(spec)
+    h = RNG.standard_normal((2, spec.d_model))
+    q, gate, _, _ = oracle.project_qkv(h, w, spec, [0, 1])
+    qw = spec.n_heads * spec.head_dim
+    np.testing.assert_allclose(q.reshape(2, -1), h @ w["wq"][:qw].T, rtol=1e-13)
+    np.testing.assert_allclose(gate.reshape(2, -1), h @ w["wq"][qw:].T, rtol=1e-13)
+
+
+def test_bias_then_qk_norm_then_rope_order():
+    spec = Spec(qkv_bias=True, qk_norm=True)
+    w = rand_layer(spec)
+    w["wk"][:] = 0.0                      # k before the norm is the bias alone
+    h = RNG.standard_normal((3, spec.d_model))
+    S = 4
+    _, _, k, _ = oracle.project_qkv(h, w, spec, S + np.arange(3))
+    kb = w["bk"].reshape(spec.n_kv_heads, spec.head_dim)
+    normed = kb / np.sqrt(np.mean(kb ** 2, axis=-1, keepdims=True) + spec.rms_eps) * w["k_norm"]
+    want = oracle.apply_rope(np.broadcast_to(normed, (3,) + normed.shape), S + np.arange(3), 1e4)
+    np.testing.assert_allclose(k, want, rtol=1e-13)
+
+
+def test_positions_from_one_hot_key_rows():
+    # k of head 0 before RoPE is e_0, so its row reveals the angle start_pos + b
+    spec = Spec(n_heads=2, n_kv_heads=1, head_dim=4, d_model=8, rope_theta=1e4)
+    w = rand_layer(spec)
+    w["wk"][:] = 0.0
+    w["wk"][0, :] = 1.0
+    x = np.ones((6, spec.d_model))        # rms_norm(ones) * g has positive mean
+    S = 9
+    h = oracle.rms_norm(x, w["g_attn"], spec.rms_eps)
+    amp = float(h[0].sum())
+    _, k_rows, _ = oracle.dense_layer(x, w, spec, S, np.zeros((S, 4)), np.zeros((S, 4)))
+    for b in range(6):
+        np.testing.assert_allclose(k_rows[b] / amp, [math.cos(S + b), 0, math.sin(S + b), 0],
+                                   atol=1e-12)
+
+
+def test_layer_residual_structure():
+    spec = Spec()
+    w = rand_layer(spec)
+    x = RNG.standard_normal((3, spec.d_model))
+    z = dict(w, wo=np.zeros_like(w["wo"]), wd=np.zeros_like(w["wd"]))
+    out, _, _ = oracle.dense_layer(x, z, spec, 0)
+    assert np.array_equal(out, x)
+    # one token and no prefix: attention returns v, so the layer has a closed form
+    spec1 = Spec(qkv_bias=True)
+    w = rand_layer(spec1)
+    x = RNG.standard_normal((1, spec1.d_model))
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    h = F.rms_norm(t(x), (spec1.d_model,), t(w["g_attn"]), eps=spec1.rms_eps)
+    v = h @ t(w["wv"]).T + t(w["bv"])
+    o = v.reshape(1, spec1.n_kv_heads, spec1.head_dim).repeat_interleave(2, dim=1).reshape(1, -1)
+    x1 = t(x) + o @ t(w["wo"]).T
+    h2 = F.rms_norm(x1, (spec1.d_model,), t(w["g_ffn"]), eps=spec1.rms_eps)
+    want = x1 + (F.silu(h2 @ t(w["wg"]).T) * (h2 @ t(w["wu"]).T)) @ t(w["wd"]).T
+    got, _, v_rows = oracle.dense_layer(x, w, spec1, 0)
+    np.testing.assert_allclose(got, want.numpy(), rtol=1e-12)
+    np.testing.assert_allclose(v_rows, v.numpy(), rtol=1e-13)
+
+
+def test_returned_rows_are_rotated_k_and_v():
+    spec = Spec(qk_norm=True, qkv_bias=True)
+    w = rand_layer(spec)
+    x = RNG.standard_normal((5, spec.d_model))
+    S = 3
+    pk, pv = RNG.standard_normal((S, 16)), RNG.standard_normal((S, 16))
+    _, k_rows, v_rows = oracle.dense_layer(x, w, spec, S, pk, pv)
+    h = oracle.rms_norm(x, w["g_attn"], spec.rms_eps)
+    k = (h @ w["wk"].T + w["bk"]).reshape(5, 2, 8)
+    k = k / np.sqrt(np.mean(k * k, -1, keepdims=True) + spec.rms_eps) * w["k_norm"]
+    z = (k[..., :4] + 1j * k[..., 4:]) * np.exp(
+        1j * (S + np.arange(5))[:, None, None] * (1e4 ** (-np.arange(4) / 4))[None, None, :])
+    np.testing.assert_allclose(k_rows.reshape(5, 2, 8), np.concatenate([z.real, z.imag], -1),
+                               rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(v_rows, h @ w["wv"].T + w["bv"], rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# invariants of the stack
+
+
+def _stack(spec, n_layers, rng=RNG):
+    return [rand_layer(spec, rng=rng) for _ in range(n_layers)]
+
+
+@pytest.mark.parametrize("extras", [dict(), dict(qkv_bias=True, qk_norm=True, softcap=3.0,
+                                                  gated=True)])
+def test_prefill_equals_single_token_steps(extras):
+    spec = Spec(**extras)
+    layers = _stack(spec, 3)
+    N = 6
+    x = RNG.standard_normal((N, spec.d_model))
+    full, fk, fv = oracle.prefill_dense_stack(x, layers, spec, 0)
+    ck = [np.zeros((0, 16)) for _ in layers]
+    cv = [np.zeros((0, 16)) for _ in layers]
+    for t in range(N):
+        out, k, v = oracle.prefill_dense_stack(x[t:t + 1], layers, spec, t, ck, cv)
+        np.testing.assert_allclose(out[0], full[t], rtol=1e-12, atol=1e-12)
+        ck = [np.concatenate([a, b]) for a, b in zip(ck, k)]
+        cv = [np.concatenate([a, b]) for a, b in zip(cv, v)]
+    for l in range(3):
+        np.testing.assert_allclose(ck[l], fk[l], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(cv[l], fv[l], rtol=1e-12, atol=1e-13)
+
+
+def test_chunked_prefill_equals_whole():
+    spec = Spec(qk_norm=True)
+    layers = _stack(spec, 2)
+    x = RNG.standard_normal((7, spec.d_model))
+    full, fk, fv = oracle.prefill_dense_stack(x, layers, spec, 0)
+    a, ak, av = oracle.prefill_dense_stack(x[:3], layers, spec, 0)
+    b, bk, bv = oracle.prefill_dense_stack(x[3:], layers, spec, 3, ak, av)
+    np.testing.assert_allclose(np.concatenate([a, b]), full, rtol=1e-12, atol=1e-12)
+    for l in range(2):
+        np.testing.assert_allclose(np.concatenate([ak[l], bk[l]]), fk[l], rtol=1e-12, atol=1e-13)
+
+
+def test_causality_later_tokens_do_not_change_earlier():
+    spec = Spec()
+    layers = _stack(spec, 2)
+    x = RNG.standard_normal((6, spec.d_model))
+    y = x.copy(); y[4:] += 5.0
+    a, ak, _ = oracle.prefill_dense_stack(x, layers, spec, 0)
+    b, bk, _ = oracle.prefill_dense_stack(y, layers, spec, 0)
+    assert np.array_equal(a[:4], b[:4]) and np.array_equal(ak[1][:4], bk[1][:4])
+    assert not np.allclose(a[4:], b[4:])
+
+
+def test_decode_attn_layer_equals_prefill_of_one_token():
+    spec = Spec(gated=True, softcap=4.0, qk_norm=True)
+    w = rand_layer(spec)
+    R = 5
+    ck, cv = RNG.standard_normal((R, 16)), RNG.standard_normal((R, 16))
+    x = RNG.standard_normal((1, spec.d_model))
+    want, k_row, v_row = oracle.dense_layer(x, w, spec, R, ck, cv)
+    h = oracle.rms_norm(x, w["g_attn"], spec.rms_eps)
+    q, gate, k, v = oracle.project_qkv(h, w, spec, [R])
+    np.testing.assert_allclose(k.reshape(-1), k_row[0], rtol=1e-14)
+    # the mirror may be bigger than the rows in use: only `rows` are read
+    big_k = np.concatenate([ck, RNG.standard_normal((3, 16))])
+    big_v = np.concatenate([cv, RNG.standard_normal((3, 16))])
+    got = oracle.attn_layer(q.reshape(-1), k.reshape(-1), v.reshape(-1), gate.reshape(-1),
+                            big_k, big_v, R, w, spec, x[0])
+    np.testing.assert_allclose(got, want[0], rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# the input encoder
+
+
+def test_bf16_encoder_matches_torch_rne():
+    x = (RNG.standard_normal(100000) * 0.02).astype(np.float32)
+    x[:4] = [1.00390625, 1.01171875, -1.00390625, 0.0]   # exact ties round to even
+    bits = synth.to_bf16_bits(x)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bits, want)
+    assert np.array_equal(synth.bf16_bits_to_f32(bits),
+                          torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_synthetic_draws_are_keyed_and_repeatable():
+    cfg = synth.STACK_CONFIGS["tiny"]
+    a = synth.layer_weights(cfg, 1)
+    b = synth.layer_weights(cfg, 1)
+    assert all(np.array_equal(a[n], b[n]) for n in a)
+    c = synth.layer_weights(cfg, 0)
+    assert not np.array_equal(a["wq"], c["wq"])
+    assert a["wq"].shape == (256, 256) and a["wg"].shape == (704, 256)
+    assert abs(float(np.std(a["wg"])) - 0.02) < 1e-3
+    assert abs(float(np.mean(a["g_attn"])) - 1.0) < 1e-2
+
+
+def test_tiny_stack_matches_committed_sample():
+    """Regression pin: the oracle still gives the committed tiny-stack sample."""
+    import importlib.util
+    import json
+    import os
+    here = os.path.join(os.path.dirname(__file__), "golden")
+    with open(os.path.join(here, "tiny_stack_sample.json")) as f:
+        want = json.load(f)
+    spec = importlib.util.spec_from_file_location("mk", os.path.join(here, "make_tiny_golden.py"))
+    mk = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mk)
+    got = mk.sample()
+    for key in ("hidden_out", "k_rows_layer1", "v_rows_layer0"):
+        np.testing.assert_allclose(got[key], want[key], rtol=1e-12, atol=1e-14)
