@@ -1,0 +1,102 @@
+"""ctypes declarations of libddl.so (include/ddl.h).  Loading fails loudly
+when the library has not been built: there is no fallback path."""
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_double, c_float, c_int, c_size_t, c_void_p
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libddl.so")
+
+DDL_DECLINED = 0
+DDL_ERR_INVALID = -1
+DDL_ERR_DEVICE = -2
+DDL_ERR_INJECTED = -3
+DDL_ERR_WORKSPACE = -4
+DDL_ACT_SWIGLU, DDL_ACT_GELU = 0, 1
+DDL_ROPE_NEOX, DDL_ROPE_NORM = 0, 1
+DDL_DTYPE_F32, DDL_DTYPE_BF16 = 0, 1
+(DDL_K_RMSNORM, DDL_K_GEMM_QKV, DDL_K_QKV_POST, DDL_K_ATTN_PREFILL, DDL_K_GEMM_WO,
+ DDL_K_GEMM_GATE_UP, DDL_K_GEMM_DOWN, DDL_K_DECODE_ATTN, DDL_K_GEMV_WO, DDL_K_GEMV_GATE_UP,
+ DDL_K_GEMV_DOWN) = range(11)
+
+
+class CtxOpts(ctypes.Structure):
+    _fields_ = [("min_batch", c_int), ("fault_after_admission", c_int)]
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [
+        ("d_model", c_int), ("n_heads", c_int), ("n_kv_heads", c_int), ("head_dim", c_int),
+        ("v_head_dim", c_int), ("d_ff", c_int),
+        ("rms_eps", c_float), ("post_norm_eps", c_float),
+        ("act", c_int),
+        ("rope_enabled", c_int), ("rope_theta", c_double), ("rope_layout", c_int),
+        ("rope_rot_dim", c_int), ("rope_mscale", c_float), ("rope_freq_factors", c_void_p),
+        ("attn_softcap", c_float),
+        ("gated", c_int), ("has_qkv_bias", c_int), ("has_qk_norm", c_int),
+        ("window", c_int),
+        ("has_post_attn_norm", c_int), ("has_post_ffn_norm", c_int), ("has_sinks", c_int),
+        ("has_alibi", c_int), ("has_lora", c_int),
+    ]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [
+        ("dtype", c_int),
+        ("wq", c_void_p), ("wk", c_void_p), ("wv", c_void_p), ("wo", c_void_p),
+        ("wg", c_void_p), ("wu", c_void_p), ("wd", c_void_p),
+        ("g_attn", c_void_p), ("g_ffn", c_void_p),
+        ("bq", c_void_p), ("bk", c_void_p), ("bv", c_void_p),
+        ("q_norm", c_void_p), ("k_norm", c_void_p),
+    ]
+
+
+# name -> (restype, argtypes); the order follows include/ddl.h
+SIGNATURES = {
+    "ddl_ctx_create": (c_void_p, [POINTER(CtxOpts)]),
+    "ddl_ctx_destroy": (None, [c_void_p]),
+    "ddl_layer_supported": (c_int, [POINTER(LayerDesc)]),
+    "ddl_layer_blob_bytes": (c_size_t, [POINTER(LayerDesc)]),
+    "ddl_layer_pack": (c_int, [c_void_p, POINTER(LayerDesc), POINTER(LayerWeights), c_void_p,
+                               c_size_t, c_void_p, POINTER(c_void_p)]),
+    "ddl_layer_destroy": (None, [c_void_p]),
+    "ddl_workspace_bytes": (c_size_t, [POINTER(c_void_p), c_int, c_int]),
+    "ddl_prefill_dense_stack": (c_int, [
+        c_void_p, c_void_p, POINTER(c_void_p), c_int, c_int, c_int,
+        POINTER(c_void_p), POINTER(c_void_p), POINTER(c_int), c_void_p,
+        POINTER(c_void_p), POINTER(c_void_p), c_void_p, c_size_t, c_void_p]),
+    "ddl_mirror_bytes": (c_size_t, [c_int, c_int, c_int]),
+    "ddl_mirror_init": (c_int, [POINTER(c_void_p), c_void_p, c_size_t, c_int, c_int, c_int]),
+    "ddl_mirror_upload": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_void_p]),
+    "ddl_mirror_seq_len": (c_int, [c_void_p]),
+    "ddl_mirror_capacity": (c_int, [c_void_p]),
+    "ddl_mirror_invalidate": (None, [c_void_p]),
+    "ddl_mirror_plan_capacity": (c_int, [c_int, c_int]),
+    "ddl_mirror_destroy": (None, [c_void_p]),
+    "ddl_attn_workspace_bytes": (c_size_t, [c_void_p, c_int]),
+    "ddl_attn_layer": (c_int, [
+        c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_float,
+        c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "ddl_probe_enable": (c_int, [c_void_p, c_int, c_int]),
+    "ddl_probe_read": (c_int, [c_void_p, POINTER(c_float), c_int]),
+    "ddl_last_error": (c_char_p, []),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                f"g.build()'` (or python dense_decoder_layer_amd/build.py)")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib

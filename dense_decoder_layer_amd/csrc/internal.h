@@ -1,0 +1,158 @@
+// Host-side structures of the library and the kernel launchers' signatures.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ddl.h"
+
+typedef _Float16 f16;
+
+#include <vector>
+
+struct ddl_ctx {
+    int min_batch;
+    int fault_after_admission;
+    // launch timing probe
+    int probe_kind = -1, probe_max = 0, probe_count = 0;
+    std::vector<hipEvent_t> probe_events;   // 2 per launch: start, end
+};
+
+// Brackets one launch of class `kind` with probe events when enabled.
+struct ProbeScope {
+    ddl_ctx* c;
+    hipStream_t s;
+    int slot = -1;
+    ProbeScope(ddl_ctx* ctx, int kind, hipStream_t stream) : c(ctx), s(stream) {
+        if (c->probe_kind == kind && c->probe_count < c->probe_max) {
+            slot = c->probe_count++;
+            hipEventRecord(c->probe_events[2 * slot], s);
+        }
+    }
+    ~ProbeScope() {
+        if (slot >= 0) hipEventRecord(c->probe_events[2 * slot + 1], s);
+    }
+};
+
+// Device header at the start of a packed layer blob.  absmax_bits are
+// filled by the pack kernels (max |w| of each packed matrix, as the bits
+// of a non-negative float so an integer max is exact); shift/inv_scale
+// are derived from them: a matrix is stored as fp16(w * 2^shift) and the
+// GEMM epilogue multiplies by inv_scale = 2^-shift.
+enum { MAT_QKV = 0, MAT_O = 1, MAT_GU = 2, MAT_D = 3, MAT_COUNT = 4 };
+struct BlobHeader {
+    uint32_t absmax_bits[MAT_COUNT];
+    int32_t shift[MAT_COUNT];
+    float inv_scale[MAT_COUNT];
+    uint32_t pad[52];
+};
+static_assert(sizeof(BlobHeader) == 256, "header is one 256-byte line");
+
+// A packed layer: shapes plus device pointers into the caller's blob.
+//   wqkv [nqkv][d]   rows: q (hq*hd), k (hkv*hd), v (hkv*hd), gate (hq*hd, gated)
+//   wo   [d][hq*hd]
+//   wgu  [2*f][d]    gate/up interleaved in 16-row blocks: block 2j = gate
+//                    rows 16j..16j+15, block 2j+1 = up rows 16j..16j+15
+//   wd   [d][f]
+struct ddl_layer {
+    int d, hq, hkv, hd, f, nqkv;
+    int gated, has_bias, has_qk_norm, rope_on;
+    float eps, softcap;
+    double theta;
+    size_t blob_bytes;
+    BlobHeader* hdr;
+    float *g_attn, *g_ffn, *bqkv, *q_norm, *k_norm;
+    f16 *wqkv, *wo, *wgu, *wd;
+};
+
+struct ddl_mirror {
+    float* k;   // [cap][hkv*hd]
+    float* v;
+    int hkv, hd, cap, seq_len;
+};
+
+// ---- launchers (each enqueues on `s`; return hipGetLastError()) ----------
+
+enum { EPI_F32 = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+
+struct GemmArgs {
+    const f16* A; int lda;      // [M][K]
+    const f16* W; int ldw;      // [N][K]
+    int M, N, K;
+    const float* inv_scale;     // device scalar, multiplies the accumulator
+    float* C; int ldc;          // EPI_F32, EPI_RESID output
+    const float* R; int ldr;    // EPI_RESID residual input (may alias C)
+    f16* H; int ldh;            // EPI_SWIGLU output [M][N/2]
+};
+hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s);
+bool gemm_shape_ok(int M, int N, int K, int epi);
+
+hipError_t launch_rmsnorm_f16(const float* x, const float* g, f16* h, int rows, int d,
+                              float eps, hipStream_t s);
+
+hipError_t launch_rope_table(float2* tab, int batch, int start_pos, int half, int rot_dim,
+                             double theta, hipStream_t s);
+
+struct QkvPostArgs {
+    const float* qkv; int nqkv;         // [B][nqkv] GEMM output
+    const float* bias;                  // [nqkv] or null
+    const float* q_norm; const float* k_norm;   // [hd] or null
+    const float2* rope;                 // [B][hd/2] or null
+    int B, hq, hkv, hd; float eps;
+    f16* q16;                           // [B][hq*hd]
+    float* k_rows; float* v_rows;       // [B][hkv*hd]
+};
+hipError_t launch_qkv_post(const QkvPostArgs& a, hipStream_t s);
+
+struct AttnPrefillArgs {
+    const f16* q16;                      // [B][hq*hd]
+    const float* pk; const float* pv;    // [S][hkv*hd] cached rows (null when S == 0)
+    const float* nk; const float* nv;    // [B][hkv*hd] new rows
+    const float* gate; int gate_ld;      // gate (B rows, stride gate_ld) or null
+    f16* o16;                            // [B][hq*hd]
+    int B, S, hq, hkv, hd;
+    float softcap;
+};
+hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s);
+
+// packing
+hipError_t launch_absmax(const void* src, int dtype, size_t n, uint32_t* out_bits,
+                         hipStream_t s);
+hipError_t launch_finalize_scales(BlobHeader* hdr, hipStream_t s);
+// Converts a [rows][cols] matrix into fp16 rows of dst (row stride cols):
+// mode 0: dst row = row_offset + r; mode 1/2: gate/up interleave (gate / up).
+hipError_t launch_convert_rows(const void* src, int dtype, int rows, int cols, f16* dst,
+                               int row_offset, int mode, const BlobHeader* hdr, int mat,
+                               hipStream_t s);
+
+// decode (one token against the mirror)
+constexpr int DECODE_MAX_SPLITS = 256;
+struct DecodeAttnArgs {
+    const float* q;                      // [hq*hd]
+    const float* knew; const float* vnew; // [hkv*hd] this token's rows
+    float* mk; float* mv;                // mirror [cap][hkv*hd]; row R is written
+    const float* gate;                   // [hq*hd] or null
+    float* part_m; float* part_l;        // [hq][n_splits]
+    float* part_o;                       // [hq][n_splits][hd]
+    float* o;                            // [hq*hd] merged, normalised, gated
+    int R, hq, hkv, hd;
+    int n_splits, rows_per_split;
+    float softcap;
+};
+bool decode_group_ok(int hq, int hkv, int hd);
+void decode_split_plan(int rows_total, int* n_splits, int* rows_per_split);
+hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s);
+
+enum { GV_RESID = 0, GV_SWIGLU = 1 };
+struct GemvArgs {
+    const f16* W; int K;         // [rows][K] packed weights (gate/up interleaved for GV_SWIGLU)
+    int N;                       // outputs
+    const float* inv_scale;      // device scalar
+    const float* x;              // [K]
+    const float* norm_g; float eps;   // RMS-norm x first when norm_g != null
+    const float* r;              // [N] residual (GV_RESID)
+    float* y;                    // [N]
+};
+bool gemv_shape_ok(int K);
+hipError_t launch_gemv(const GemvArgs& a, int epi, hipStream_t s);

@@ -1,0 +1,172 @@
+"""GPU parity of ddl_attn_layer (one token against the device KV mirror)
+with the CPU oracle, and the mirror's staleness and capacity rules, through
+the C ABI.  The output hidden must match within relative L2 1e-2; the
+appended mirror row, seq_len and declines are exact."""
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+
+def rel(a, b) -> float:
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(np.asarray(a, np.float64) - b) / np.linalg.norm(b))
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def ddl():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dense_decoder_layer_amd as m
+    return m
+
+
+class Decode:
+    """A packed layer, a mirror sized by the capacity policy, and buffers."""
+
+    def __init__(self, ddl, cfg, inputs, ctx=None, planned=0):
+        from dense_decoder_layer_amd.workloads import desc_for
+        self.ddl, self.cfg, self.inp = ddl, cfg, inputs
+        self.ctx = ctx or ddl.ddl_ctx_create()
+        self.layer = ddl.pack_layer_from_host(self.ctx, desc_for(cfg.stack_view()),
+                                              inputs["weights"])
+        self.cap = ddl.ddl_mirror_plan_capacity(cfg.rows, planned)
+        self.buf = torch.empty(ddl.ddl_mirror_bytes(cfg.n_kv_heads, cfg.head_dim, self.cap),
+                               dtype=torch.uint8, device="cuda")
+        self.mirror = ddl.ddl_mirror_init(self.buf, cfg.n_kv_heads, cfg.head_dim, self.cap)
+        self.ws = torch.empty(ddl.ddl_attn_workspace_bytes(self.layer, self.cap),
+                              dtype=torch.uint8, device="cuda")
+        self.out = torch.empty(cfg.d_model, dtype=torch.float32, device="cuda")
+
+    def upload(self, k, v, rows):
+        return self.ddl.ddl_mirror_upload(self.mirror, torch.from_numpy(k).cuda(),
+                                          torch.from_numpy(v).cuda(), rows)
+
+    def step(self, rows, q, k, v, gate, residual, ctx=None):
+        t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        rc = self.ddl.ddl_attn_layer(ctx or self.ctx, self.mirror, rows, t(q), t(k), t(v),
+                                     t(gate), self.cfg.n_heads, self.cfg.softcap, self.layer,
+                                     t(residual), self.out, self.ws)
+        torch.cuda.synchronize()
+        return rc
+
+    def mirror_rows(self, rows):
+        kvw = self.cfg.kv_width
+        flat = self.buf.view(torch.float32)
+        half = flat.numel() // 2
+        return (flat[: rows * kvw].view(rows, kvw).cpu().numpy(),
+                flat[half: half + rows * kvw].view(rows, kvw).cpu().numpy())
+
+
+def weights_values(inp):
+    return {n: synth.values(a) for n, a in inp["weights"].items()}
+
+
+@pytest.mark.parametrize("rows", synth.DECODE_ROWS)
+def test_decode_layer_matches_oracle(ddl, rows):
+    cfg = synth.DECODE_CONFIG.replace(rows=rows)
+    say(f"decode rows={rows} hq={cfg.n_heads} hkv={cfg.n_kv_heads} d={cfg.d_model} f={cfg.d_ff}")
+    inp = synth.decode_inputs(cfg)
+    dec = Decode(ddl, cfg, inp)
+    assert dec.upload(inp["cache_k"], inp["cache_v"], rows) == 1
+    assert ddl.ddl_mirror_seq_len(dec.mirror) == rows
+    rc = dec.step(rows, inp["q"], inp["k"], inp["v"], inp["gate"], inp["residual"])
+    assert rc == 1, ddl.ddl_last_error()
+    assert ddl.ddl_mirror_seq_len(dec.mirror) == rows + 1
+    mk, mv = dec.mirror_rows(rows + 1)
+    assert np.array_equal(mk[rows], inp["k"]) and np.array_equal(mv[rows], inp["v"])
+    assert np.array_equal(mk[:rows], inp["cache_k"]) and np.array_equal(mv[:rows], inp["cache_v"])
+    t0 = time.time()
+    want = oracle.attn_layer(inp["q"], inp["k"], inp["v"], inp["gate"], inp["cache_k"],
+                             inp["cache_v"], rows, weights_values(inp), cfg, inp["residual"])
+    err = rel(dec.out.cpu().numpy(), want)
+    say(f"  oracle {time.time() - t0:.1f}s out rel L2 {err:.2e}")
+    assert err <= TOL
+
+
+def small_cfg(**kw):
+    base = dict(name="small-decode", d_model=512, n_heads=8, n_kv_heads=2, head_dim=128,
+                d_ff=1024, rows=100, softcap=0.0, gated=False)
+    base.update(kw)
+    return synth.DecodeConfig(**base)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(gated=True, softcap=2.0),
+                                dict(n_heads=4, n_kv_heads=4, head_dim=64, rows=0),
+                                dict(n_heads=6, n_kv_heads=2, rows=1000, weight_dtype="fp32"),
+                                dict(n_heads=16, n_kv_heads=2, rows=17)])
+def test_decode_shapes(ddl, kw):
+    cfg = small_cfg(**kw)
+    inp = synth.decode_inputs(cfg)
+    dec = Decode(ddl, cfg, inp)
+    dec.upload(inp["cache_k"], inp["cache_v"], cfg.rows)
+    gate = inp["gate"] if cfg.gated else None
+    assert dec.step(cfg.rows, inp["q"], inp["k"], inp["v"], gate, inp["residual"]) == 1
+    want = oracle.attn_layer(inp["q"], inp["k"], inp["v"], gate, inp["cache_k"], inp["cache_v"],
+                             cfg.rows, weights_values(inp), cfg, inp["residual"])
+    err = rel(dec.out.cpu().numpy(), want)
+    say(f"decode {kw}: out rel L2 {err:.2e}")
+    assert err <= TOL
+
+
+def test_decode_chain_and_mirror_rules(ddl):
+    cfg = small_cfg(rows=40, gated=True, softcap=50.0)
+    inp = synth.decode_inputs(cfg)
+    dec = Decode(ddl, cfg, inp)
+    w = weights_values(inp)
+    host_k, host_v = inp["cache_k"].copy(), inp["cache_v"].copy()
+    rng = np.random.default_rng(5)
+    # stale mirror (never uploaded: seq_len 0 != 40) declines and touches nothing
+    assert dec.step(40, inp["q"], inp["k"], inp["v"], inp["gate"], inp["residual"]) == 0
+    assert ddl.ddl_mirror_seq_len(dec.mirror) == 0 and "stale" in ddl.ddl_last_error()
+    dec.upload(host_k, host_v, 40)
+    for step in range(4):
+        rows = host_k.shape[0]
+        q, k, v, gate, x = (rng.standard_normal(n).astype(np.float32) for n in
+                            (cfg.q_width, cfg.kv_width, cfg.kv_width, cfg.q_width, cfg.d_model))
+        assert dec.step(rows, q, k, v, gate, x) == 1, ddl.ddl_last_error()
+        want = oracle.attn_layer(q, k, v, gate, host_k, host_v, rows, w, cfg, x)
+        assert rel(dec.out.cpu().numpy(), want) <= TOL
+        host_k, host_v = np.vstack([host_k, k]), np.vstack([host_v, v])   # the caller's push
+        assert ddl.ddl_mirror_seq_len(dec.mirror) == host_k.shape[0]
+    # the host cache moves backwards: the mirror is stale, declines, re-uploads
+    host_k, host_v = host_k[:30], host_v[:30]
+    assert dec.step(30, inp["q"], inp["k"], inp["v"], inp["gate"], inp["residual"]) == 0
+    dec.upload(host_k, host_v, 30)
+    assert dec.step(30, inp["q"], inp["k"], inp["v"], inp["gate"], inp["residual"]) == 1
+    want = oracle.attn_layer(inp["q"], inp["k"], inp["v"], inp["gate"], host_k, host_v, 30, w,
+                             cfg, inp["residual"])
+    assert rel(dec.out.cpu().numpy(), want) <= TOL
+    # an injected failure after admission marks the mirror stale
+    fctx = ddl.ddl_ctx_create(fault_after_admission=True)
+    with pytest.raises(RuntimeError, match="-3"):
+        dec.step(31, inp["q"], inp["k"], inp["v"], inp["gate"], inp["residual"], ctx=fctx)
+    assert ddl.ddl_mirror_seq_len(dec.mirror) == -1
+
+
+def test_capacity_rule(ddl):
+    cfg = small_cfg(rows=511)
+    inp = synth.decode_inputs(cfg)
+    dec = Decode(ddl, cfg, inp)
+    assert dec.cap == 512
+    dec.upload(inp["cache_k"], inp["cache_v"], 511)
+    assert dec.step(511, inp["q"], inp["k"], inp["v"], None, inp["residual"]) == 1
+    # 512 rows fill the mirror: the next token needs a bigger one
+    assert dec.step(512, inp["q"], inp["k"], inp["v"], None, inp["residual"]) == 0
+    assert "capacity" in ddl.ddl_last_error()
+    assert ddl.ddl_mirror_plan_capacity(512) == 1024
+    assert ddl.ddl_mirror_plan_capacity(512, 2048) == 2048

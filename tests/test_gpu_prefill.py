@@ -1,0 +1,219 @@
+"""GPU parity of ddl_prefill_dense_stack against the CPU oracle, on the same
+seeded inputs, through the C ABI.  Tolerances (relative L2 over each array):
+K/V rows of every layer <= 5e-3, final hidden <= 1e-2; run lengths, row
+counts and declines exact."""
+import os
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+KV_TOL, HIDDEN_TOL = 5e-3, 1e-2
+
+
+def rel(a, b) -> float:
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(np.asarray(a, np.float64) - b) / np.linalg.norm(b))
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def ddl():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dense_decoder_layer_amd as m
+    return m
+
+
+def host_values(layers):
+    for w in layers:
+        yield {n: synth.values(a) for n, a in w.items()}
+
+
+def gpu_run(ddl, cfg, inp, min_batch=1, hidden=None):
+    from dense_decoder_layer_amd.workloads import DeviceStack
+    ctx = ddl.ddl_ctx_create(min_batch=min_batch)
+    stack = DeviceStack(ctx, cfg, inp.layers)
+    bufs = stack.buffers(cfg.batch)
+    h = torch.from_numpy(inp.hidden if hidden is None else hidden).cuda()
+    pk = [torch.from_numpy(a).cuda() for a in inp.prefix_k] if cfg.start_pos else None
+    pv = [torch.from_numpy(a).cuda() for a in inp.prefix_v] if cfg.start_pos else None
+    run = stack.run(h, cfg.start_pos, pk, pv, bufs)
+    torch.cuda.synchronize()
+    out = bufs["hidden_out"].cpu().numpy()
+    ks = [t.cpu().numpy() for t in bufs["k_rows"]]
+    vs = [t.cpu().numpy() for t in bufs["v_rows"]]
+    return run, out, ks, vs
+
+
+def check_parity(name, cfg, inp, got, n_layers):
+    run, out, ks, vs = got
+    assert run == n_layers
+    t0 = time.time()
+    want, wk, wv = oracle.prefill_dense_stack(inp.hidden, host_values(inp.layers), cfg,
+                                              cfg.start_pos, inp.prefix_k, inp.prefix_v)
+    kv = [(rel(ks[l], wk[l]), rel(vs[l], wv[l])) for l in range(n_layers)]
+    worst_kv = max(max(a, b) for a, b in kv)
+    err_h = rel(out, want)
+    row_err = np.linalg.norm(out - want, axis=1) / np.linalg.norm(want, axis=1)
+    say(f"[{name}] oracle {time.time() - t0:.1f}s  K/V rel L2 max {worst_kv:.2e} "
+        f"(layer0 {kv[0][0]:.2e}/{kv[0][1]:.2e}, last {kv[-1][0]:.2e}/{kv[-1][1]:.2e})  "
+        f"hidden rel L2 {err_h:.2e}  worst token row {row_err.max():.2e}")
+    assert ks[0].shape == (cfg.batch, cfg.kv_width)
+    assert np.isfinite(out).all()
+    assert worst_kv <= KV_TOL, kv
+    assert err_h <= HIDDEN_TOL
+
+
+def small(name, **kw):
+    base = dict(name=name, n_layers=2, d_model=512, n_heads=8, n_kv_heads=2, head_dim=128,
+                d_ff=1024, batch=150, start_pos=0, rope_theta=5e5, weight_dtype="bf16")
+    base.update(kw)
+    return synth.StackConfig(**base)
+
+
+SMALL_CASES = {
+    "tiny": synth.STACK_CONFIGS["tiny"],
+    "tiny-b1": synth.STACK_CONFIGS["tiny"].replace(batch=1),
+    "tiny-b3": synth.STACK_CONFIGS["tiny"].replace(batch=3),
+    "tiny-b200-prefix37": synth.STACK_CONFIGS["tiny"].replace(batch=200, start_pos=37),
+    "hd128-b150": small("hd128-b150"),
+    "hd128-prefix100-b77": small("hd128-prefix100-b77", batch=77, start_pos=100),
+    "hd128-extras": small("hd128-extras", batch=65, start_pos=37, qkv_bias=True, qk_norm=True,
+                          softcap=30.0, gated=True, n_layers=3),
+    "mha-hd64": small("mha-hd64", n_heads=4, n_kv_heads=4, head_dim=64, batch=130),
+    "group4-hd128": small("group4-hd128", n_heads=16, n_kv_heads=4, d_model=1024, batch=129,
+                          start_pos=200, d_ff=2816),
+    "group3-fp32": small("group3-fp32", n_heads=6, n_kv_heads=2, d_model=768, batch=96,
+                         weight_dtype="fp32", softcap=5.0),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL_CASES))
+def test_small_stacks_match_oracle(ddl, name):
+    cfg = SMALL_CASES[name]
+    say(f"case {name}: B={cfg.batch} S={cfg.start_pos} L={cfg.n_layers} d={cfg.d_model} "
+        f"heads={cfg.n_heads}/{cfg.n_kv_heads}x{cfg.head_dim}")
+    inp = synth.stack_inputs(cfg)
+    check_parity(name, cfg, inp, gpu_run(ddl, cfg, inp), cfg.n_layers)
+
+
+def test_deterministic_and_causal(ddl):
+    cfg = small("causal", batch=140, start_pos=20, softcap=20.0, gated=True)
+    inp = synth.stack_inputs(cfg)
+    a = gpu_run(ddl, cfg, inp)
+    b = gpu_run(ddl, cfg, inp)
+    assert np.array_equal(a[1], b[1]) and all(np.array_equal(x, y) for x, y in zip(a[2], b[2]))
+    cut = 70
+    pert = inp.hidden.copy()
+    pert[cut:] += np.float32(3.0)
+    c = gpu_run(ddl, cfg, inp, hidden=pert)
+    assert np.array_equal(a[1][:cut], c[1][:cut])
+    for l in range(cfg.n_layers):
+        assert np.array_equal(a[2][l][:cut], c[2][l][:cut])
+        assert np.array_equal(a[3][l][:cut], c[3][l][:cut])
+    assert not np.allclose(a[1][cut:], c[1][cut:])
+
+
+def test_position_zero_k_rows_are_unrotated(ddl):
+    # with no prefix, token 0 sits at position 0 where RoPE is the identity:
+    # its K row equals the same layer run without RoPE
+    cfg = small("pos0", batch=4)
+    inp = synth.stack_inputs(cfg)
+    rot = gpu_run(ddl, cfg, inp)
+    flat = gpu_run(ddl, cfg.replace(rope_theta=None), inp)
+    assert np.array_equal(rot[2][0][0], flat[2][0][0])
+    assert not np.array_equal(rot[2][0][1], flat[2][0][1])
+
+
+def _sentinel_bufs(stack, batch):
+    bufs = stack.buffers(batch)
+    bufs["hidden_out"].fill_(7.0)
+    for t in bufs["k_rows"] + bufs["v_rows"]:
+        t.fill_(7.0)
+    return bufs
+
+
+def test_declines_touch_nothing_and_runs_stop_at_ineligible_layer(ddl):
+    from dense_decoder_layer_amd.workloads import DeviceStack
+    cfg = synth.STACK_CONFIGS["tiny"].replace(n_layers=3)
+    inp = synth.stack_inputs(cfg)
+    ctx = ddl.ddl_ctx_create()                   # min_batch 4
+    stack = DeviceStack(ctx, cfg, inp.layers)
+    h = torch.from_numpy(inp.hidden).cuda()
+    untouched = lambda bufs, n: (bool((bufs["hidden_out"] == 7.0).all()) and
+                                 all(bool((t == 7.0).all()) for t in bufs["k_rows"][:n]))
+    # batch below min_batch
+    bufs = _sentinel_bufs(stack, 3)
+    assert stack.run(h[:3], 0, None, None, bufs) == ddl.DDL_DECLINED
+    torch.cuda.synchronize()
+    assert untouched(bufs, 3) and "min_batch" in ddl.ddl_last_error()
+    # layer 0's cache rows differ from start_pos
+    bufs = _sentinel_bufs(stack, 8)
+    assert stack.run(h, 0, None, None, bufs, prefix_rows=[5, 0, 0]) == ddl.DDL_DECLINED
+    torch.cuda.synchronize()
+    assert untouched(bufs, 3)
+    # layer 2 ineligible: the run is layers 0..1, layer 2's rows untouched
+    bufs = _sentinel_bufs(stack, 8)
+    assert stack.run(h, 0, None, None, bufs, prefix_rows=[0, 0, 9]) == 2
+    torch.cuda.synchronize()
+    assert bool((bufs["k_rows"][2] == 7.0).all()) and not bool((bufs["k_rows"][1] == 7.0).all())
+    want, wk, _ = oracle.prefill_dense_stack(inp.hidden, list(host_values(inp.layers))[:2], cfg, 0)
+    assert rel(bufs["hidden_out"].cpu().numpy(), want) <= HIDDEN_TOL
+    # an injected failure after admission: error, nothing written
+    fctx = ddl.ddl_ctx_create(fault_after_admission=True)
+    bufs = _sentinel_bufs(stack, 8)
+    with pytest.raises(RuntimeError, match="-3"):
+        ddl.ddl_prefill_dense_stack(fctx, h, stack.layers, 0, None, None, [0, 0, 0],
+                                    bufs["hidden_out"], bufs["k_rows"], bufs["v_rows"],
+                                    bufs["workspace"])
+    torch.cuda.synchronize()
+    assert untouched(bufs, 3)
+    # workspace too small
+    bufs = _sentinel_bufs(stack, 8)
+    with pytest.raises(RuntimeError, match="-4"):
+        ddl.ddl_prefill_dense_stack(ctx, h, stack.layers, 0, None, None, [0, 0, 0],
+                                    bufs["hidden_out"], bufs["k_rows"], bufs["v_rows"],
+                                    bufs["workspace"][:100])
+    # a layer the kernels do not serve is declined at pack time
+    assert ddl.ddl_layer_pack(ctx, ddl.layer_desc(256, 4, 2, 64, 704, window=128), {},
+                              ddl.DDL_DTYPE_F32, bufs["workspace"]) is None
+
+
+def _full_case(ddl, name, cfg, n_layers=None):
+    t0 = time.time()
+    n = cfg.n_layers if n_layers is None else n_layers
+    say(f"[{name}] drawing inputs for {n} layers ...")
+    inp = synth.stack_inputs(cfg, n)
+    say(f"[{name}] inputs {time.time() - t0:.1f}s; packing and running on the GPU ...")
+    got = gpu_run(ddl, cfg.replace(n_layers=n), inp)
+    say(f"[{name}] GPU done {time.time() - t0:.1f}s; oracle ...")
+    check_parity(name, cfg, inp, got, n)
+
+
+@pytest.mark.timeout(900)
+def test_llama3b_pp512_full_stack(ddl):
+    _full_case(ddl, "llama3b_pp512", synth.STACK_CONFIGS["llama3b_pp512"])
+
+
+@pytest.mark.timeout(900)
+def test_llama3b_prefix1536_full_stack(ddl):
+    _full_case(ddl, "llama3b_prefix1536", synth.STACK_CONFIGS["llama3b_prefix1536"])
+
+
+@pytest.mark.timeout(900)
+def test_llama8b_pp4096_extras_first_layers(ddl):
+    # the whole 32-layer stack is ~57 TFLOP of fp64 oracle work; the first
+    # two layers at the full pp4096 shape keep the check within minutes
+    _full_case(ddl, "llama8b_pp4096_extras", synth.STACK_CONFIGS["llama8b_pp4096_extras"], 2)
