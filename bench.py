@@ -85,7 +85,7 @@ def main():
     ctx = ddl.ddl_ctx_create()
     layers_iter = (synth.layer_weights(cfg, l) for l in range(cfg.n_layers))
     stack = DeviceStack(ctx, cfg, layers_iter)
-    bufs = stack.buffers(cfg.batch)
+    bufs = stack.buffers(cfg.batch, cfg.start_pos)
     hidden = torch.from_numpy(synth.hidden_rows(cfg)).cuda()
     torch.cuda.synchronize()
     log(f"packed {cfg.n_layers} layers in {time.time() - t0:.1f}s")

@@ -193,9 +193,9 @@ def pack_layer_from_host(ctx: Ctx, desc: LayerDesc, host: Dict[str, np.ndarray],
     return layer
 
 
-def ddl_workspace_bytes(layers: Sequence[Layer], max_batch: int) -> int:
+def ddl_workspace_bytes(layers: Sequence[Layer], max_batch: int, max_start_pos: int) -> int:
     arr = (c_void_p * len(layers))(*[l.handle for l in layers])
-    return int(_lib().ddl_workspace_bytes(arr, len(layers), max_batch))
+    return int(_lib().ddl_workspace_bytes(arr, len(layers), max_batch, max_start_pos))
 
 
 def ddl_prefill_dense_stack(ctx: Ctx, hidden: torch.Tensor, layers: Sequence[Layer],

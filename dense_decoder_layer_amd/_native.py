@@ -60,7 +60,7 @@ SIGNATURES = {
     "ddl_layer_pack": (c_int, [c_void_p, POINTER(LayerDesc), POINTER(LayerWeights), c_void_p,
                                c_size_t, c_void_p, POINTER(c_void_p)]),
     "ddl_layer_destroy": (None, [c_void_p]),
-    "ddl_workspace_bytes": (c_size_t, [POINTER(c_void_p), c_int, c_int]),
+    "ddl_workspace_bytes": (c_size_t, [POINTER(c_void_p), c_int, c_int, c_int]),
     "ddl_prefill_dense_stack": (c_int, [
         c_void_p, c_void_p, POINTER(c_void_p), c_int, c_int, c_int,
         POINTER(c_void_p), POINTER(c_void_p), POINTER(c_int), c_void_p,

@@ -5,178 +5,209 @@
 // of "frink-models 0.38.0 src/decoder/device_attention.rs",
 // device_attention_layer).
 //
-// Flash-style: a 256-thread workgroup takes 64 queries of one query head
-// (16 per wave) and walks the keys in tiles of 32, keeping a running max and
-// sum per query (online softmax, base-2 exponentials).  K and V tiles are
-// read as fp32 rows -- from the caller's prefix for key j < S, from this
-// call's K/V rows after -- rounded to fp16 into LDS, K row-major and V
-// transposed.  Both products run on v_mfma_f32_16x16x32_f16 in transposed
-// form, S^T = K Q^T and O^T += V^T P^T, so every lane holds the scores and
-// the output columns of exactly one query: the softmax statistics of a query
-// live in the four lanes l, l^16, l^32, l^48 and the rescale factor is one
-// scalar per lane.  Tiles wholly above a wave's last query are skipped;
-// masked scores are -inf and contribute exact zeros, so a token's outputs do
-// not depend on the values of later tokens.
+// Flash-style, one wave per workgroup: the wave takes 32 queries of one
+// query head and walks the keys of its KV head in tiles of 32 with a running
+// max and sum per query (online softmax, base-2 exponentials).  Keys and
+// values were staged once per layer as fp16: K16 [kv head][key][hd] and
+// Vt16 [kv head][hd][key].  Tiles move global -> LDS by DMA
+// (global_load_lds_dwordx4) through a 3-stage ring, so the next tiles are in
+// flight while one is used; a single wave needs no barriers.  Both products
+// run on v_mfma_f32_32x32x16_f16 in transposed form: S^T = K Q^T gives every
+// lane 16 scores of one query (its partner lane l^32 holds the other 16), and
+// those probabilities are directly the B operand of O^T += V^T P^T; the
+// rescale factor of a query is one scalar per lane.  Tiles wholly above the
+// wave's last query are not visited; masked scores are -inf and contribute
+// exact zeros, so a token's outputs do not depend on later tokens' values.
 #include "common.h"
 #include "internal.h"
 
 namespace {
 
-constexpr int KT = 32;   // keys per tile
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+constexpr int KT = 32;    // keys per tile
+constexpr int NS = 3;     // LDS ring stages
+
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, 0);
+#endif
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 template <int HD>
-__global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs p) {
-    constexpr int HC = HD / 8;          // 16-byte chunks per K row in LDS
-    constexpr int VT_LD = KT + 4;       // V^T row stride (halves), keeps 8-byte reads aligned
-    constexpr int KS = HD / 32;         // MFMA k-steps over the head dimension
-    constexpr int HB = HD / 16;         // 16-row blocks of O^T
-    constexpr int LOADS = KT * HD / 4 / 256;
-    __shared__ half8 Ks[KT * HC];
-    __shared__ f16 Vt[HD * VT_LD];
+__global__ __launch_bounds__(64) void attn_prefill_kernel(AttnPrefillArgs p) {
+    constexpr int KCH = HD / 8;                  // 16-byte chunks per K row
+    constexpr int K_BYTES = KT * HD * 2;         // K tile [32 keys][HD]
+    constexpr int V_BYTES = HD * KT * 2;         // V^T tile [HD][32 keys]
+    constexpr int STAGE = K_BYTES + V_BYTES;
+    constexpr int K_INSTR = K_BYTES / 1024, V_INSTR = V_BYTES / 1024;
+    constexpr int PER = K_INSTR + V_INSTR;       // DMA instructions per tile
+    constexpr int KS = HD / 16;                  // k-steps of S^T over the head dim
+    constexpr int HB = HD / 32;                  // 32-row blocks of O^T
+    __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4;
-    const int qt = gridDim.x - 1 - blockIdx.x;      // longest rows first
+    const int lane = threadIdx.x, g2 = lane >> 5, ql = lane & 31;
+    const int qt = gridDim.x - 1 - blockIdx.x;     // longest rows first
     const int h = blockIdx.y;
     const int g = h / (p.hq / p.hkv);
-    const int kvw = p.hkv * HD;
-    const int q0 = qt * 64;
-    const int qrow = q0 + wave * 16 + (lane & 15);  // this lane's query token
+    const int q0 = qt * 32;
+    const int qrow = q0 + ql;                      // this lane's query token
     const int qpos = p.S + qrow;
     const int nkeys = p.S + p.B;
-    const int kv_end = min(p.S + q0 + 64, nkeys);
-    const int wave_last = p.S + q0 + wave * 16 + 15;
+    const int kv_end = min(p.S + q0 + 32, nkeys);  // keys the wave can see
+    const int ntiles = (kv_end + KT - 1) / KT;
     const float LOG2E = 1.4426950408889634f;
     const float scale = 1.0f / sqrtf((float)HD);
 
+    // Per-lane DMA sources.  K: instruction j covers rows 4j..4j+3 (HD=128)
+    // or 8j..8j+7 (HD=64); lane chunk (l % KCH) ^ (row % 8) keeps the K rows
+    // XOR-swizzled.  V^T: instruction j covers hd rows 16j..16j+15, four
+    // 16-byte chunks (8 keys) each; chunk c of row r sits at c ^ ((r/2) % 4).
+    const f16* kbase = p.k16 + (size_t)g * p.tcap * HD;
+    const f16* vbase = p.vt16 + (size_t)g * HD * p.tcap;
+    const uint32_t sm = (uint32_t)(uintptr_t)smem;
+    size_t koff[K_INSTR], voff[V_INSTR];
+#pragma unroll
+    for (int j = 0; j < K_INSTR; ++j) {
+        const int r = j * (64 / KCH) + lane / KCH;
+        koff[j] = (size_t)r * HD + (((lane % KCH) ^ (r & 7)) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < V_INSTR; ++j) {
+        const int r = j * 16 + (lane >> 2);
+        voff[j] = (size_t)r * p.tcap + (((lane & 3) ^ ((r >> 1) & 3)) * 8);
+    }
+    auto issue = [&](int tile, int slot) {
+        const uint32_t sb = sm + slot * STAGE;
+        const size_t k0 = (size_t)tile * KT;
+#pragma unroll
+        for (int j = 0; j < K_INSTR; ++j) dma16(kbase + k0 * HD + koff[j], sb + j * 1024);
+#pragma unroll
+        for (int j = 0; j < V_INSTR; ++j) dma16(vbase + k0 + voff[j], sb + K_BYTES + j * 1024);
+    };
+
+    // Q^T operand: lane holds Q[qrow][ks*16 + 8*g2 .. +7]
     half8 qf[KS];
     const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-        qf[ks] = qrow < p.B ? *reinterpret_cast<const half8*>(
-                                  p.q16 + (size_t)qrow * p.hq * HD + h * HD + ks * 32 + 8 * grp)
+        qf[ks] = qrow < p.B ? *reinterpret_cast<const half8*>(p.q16 + (size_t)qrow * p.hq * HD +
+                                                                h * HD + ks * 16 + 8 * g2)
                             : zero8;
 
-    floatx4 o[HB];
+    floatx16 o[HB];
 #pragma unroll
-    for (int i = 0; i < HB; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < HB; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
     float m = -INFINITY, l = 0.f;
 
-    for (int k0 = 0; k0 < kv_end; k0 += KT) {
-        float4 kr[LOADS], vr[LOADS];
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int idx = i * 256 + tid, key = idx / (HD / 4), c4 = idx % (HD / 4);
-            const int j = k0 + key;
-            const float* ks = nullptr;
-            const float* vs = nullptr;
-            if (j < p.S) {
-                ks = p.pk + (size_t)j * kvw;
-                vs = p.pv + (size_t)j * kvw;
-            } else if (j < nkeys) {
-                ks = p.nk + (size_t)(j - p.S) * kvw;
-                vs = p.nv + (size_t)(j - p.S) * kvw;
-            }
-            kr[i] = ks ? *reinterpret_cast<const float4*>(ks + g * HD + c4 * 4)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
-            vr[i] = vs ? *reinterpret_cast<const float4*>(vs + g * HD + c4 * 4)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        __syncthreads();   // the previous tile's readers are done
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int idx = i * 256 + tid, key = idx / (HD / 4), c4 = idx % (HD / 4);
-            half4* kd = reinterpret_cast<half4*>(&Ks[key * HC + ((c4 >> 1) ^ (key & 7))]) + (c4 & 1);
-            *kd = half4{(f16)kr[i].x, (f16)kr[i].y, (f16)kr[i].z, (f16)kr[i].w};
-            f16* vd = &Vt[(c4 * 4) * VT_LD + key];
-            vd[0] = (f16)vr[i].x;
-            vd[VT_LD] = (f16)vr[i].y;
-            vd[2 * VT_LD] = (f16)vr[i].z;
-            vd[3 * VT_LD] = (f16)vr[i].w;
-        }
-        __syncthreads();
-        if (k0 > wave_last) continue;   // wave-uniform: every key of the tile is masked
+    issue(0, 0);
+    issue(min(1, ntiles - 1), 1);
+    for (int t = 0; t < ntiles; ++t) {
+        const int slot = t % NS;
+        // the tile after next goes into the slot used two tiles ago (or the
+        // last tile again, into that already-used slot: same wait count on
+        // every path)
+        issue(min(t + 2, ntiles - 1), (t + 2) % NS);
+        wait_vmcnt<2 * PER>();            // tile t has landed in LDS
+        asm volatile("" ::: "memory");
+        const half8* Ks = reinterpret_cast<const half8*>(smem + slot * STAGE);
+        const f16* Vs = reinterpret_cast<const f16*>(smem + slot * STAGE + K_BYTES);
+        const int k0 = t * KT;
 
-        floatx4 st[2];
+        // S^T[key][query]: A = K rows, B = Q^T
+        floatx16 st;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            st[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
-            const int key = kb * 16 + (lane & 15);
+        for (int e = 0; e < 16; ++e) st[e] = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int c = ks * 4 + grp;
-                st[kb] = mfma16x16x32(Ks[key * HC + (c ^ (key & 7))], qf[ks], st[kb]);
-            }
+        for (int ks = 0; ks < KS; ++ks) {
+            const int c = ks * 2 + g2;
+            st = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ks[ql * KCH + (c ^ (ql & 7))], qf[ks], st,
+                                                        0, 0, 0);
         }
-        // lane holds S^T[key = kb*16 + 4*grp + e][query = lane & 15]
-        float s[8];
+        // lane holds key k0 + 8*(e/4) + 4*g2 + e%4 of query qrow
         float tmax = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int kpos = k0 + kb * 16 + 4 * grp + e;
-                float v = st[kb][e] * scale;
-                if (p.softcap > 0.f) v = p.softcap * tanhf(v / p.softcap);
-                v *= LOG2E;
-                if (kpos > qpos || kpos >= nkeys) v = -INFINITY;
-                s[kb * 4 + e] = v;
-                tmax = fmaxf(tmax, v);
-            }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        for (int e = 0; e < 16; ++e) {
+            const int kpos = k0 + 8 * (e >> 2) + 4 * g2 + (e & 3);
+            float v = st[e] * scale;
+            if (p.softcap > 0.f) v = p.softcap * tanhf(v / p.softcap);
+            v *= LOG2E;
+            if (kpos > qpos || kpos >= nkeys) v = -INFINITY;
+            st[e] = v;
+            tmax = fmaxf(tmax, v);
+        }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
         const float m_new = fmaxf(m, tmax);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = exp2f(m - m_use);
         float psum = 0.f;
-        half8 pf;
+        half8 pf[2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float pv = exp2f(s[i] - m_use);
+        for (int e = 0; e < 16; ++e) {
+            const float pv = exp2f(st[e] - m_use);
             psum += pv;
-            pf[i] = (f16)pv;
+            pf[e >> 3][e & 7] = (f16)pv;
         }
-        psum += __shfl_xor(psum, 16, 64);
         psum += __shfl_xor(psum, 32, 64);
         l = l * alpha + psum;
         m = m_new;
-        // P^T operand: element i of lane group grp is key (i < 4 ? 4*grp + i
-        // : 16 + 4*grp + i - 4); the V^T operand uses the same key order.
+        // O^T[hd][query] += V^T P^T.  P^T operand kh: element j of lane group
+        // g2 is key kh*16 + (j < 4 ? 4*g2 + j : 8 + 4*g2 + j - 4), which is
+        // exactly score e = 8*kh + j above; the V^T operand reads the same keys.
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
-            const f16* vrow = &Vt[(hb * 16 + (lane & 15)) * VT_LD];
-            const half4 lo = *reinterpret_cast<const half4*>(vrow + 4 * grp);
-            const half4 hi = *reinterpret_cast<const half4*>(vrow + 16 + 4 * grp);
-            const half8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            const int r = hb * 32 + ql;
+            const f16* vrow = Vs + r * KT;
+            const int sw = (r >> 1) & 3;
             o[hb] = o[hb] * alpha;
-            o[hb] = mfma16x16x32(vf, pf, o[hb]);
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                const half4 lo = *reinterpret_cast<const half4*>(vrow + (((2 * kh) ^ sw) * 8) + 4 * g2);
+                const half4 hi = *reinterpret_cast<const half4*>(vrow + (((2 * kh + 1) ^ sw) * 8) + 4 * g2);
+                const half8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                o[hb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[kh], o[hb], 0, 0, 0);
+            }
         }
     }
+    wait_vmcnt<0>();
 
     if (qrow >= p.B) return;
     const float inv_l = 1.0f / l;
     f16* dst = p.o16 + (size_t)qrow * p.hq * HD + h * HD;
     const float* gt = p.gate ? p.gate + (size_t)qrow * p.gate_ld + h * HD : nullptr;
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-        const int d0 = hb * 16 + 4 * grp;
-        float r[4];
+    for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            r[e] = o[hb][e] * inv_l;
-            if (gt) r[e] *= 1.0f / (1.0f + expf(-gt[d0 + e]));
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int d0 = hb * 32 + 8 * q4 + 4 * g2;
+            float r[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                r[e] = o[hb][q4 * 4 + e] * inv_l;
+                if (gt) r[e] *= 1.0f / (1.0f + expf(-gt[d0 + e]));
+            }
+            *reinterpret_cast<half4*>(dst + d0) = half4{(f16)r[0], (f16)r[1], (f16)r[2], (f16)r[3]};
         }
-        *reinterpret_cast<half4*>(dst + d0) = half4{(f16)r[0], (f16)r[1], (f16)r[2], (f16)r[3]};
-    }
 }
 
 }  // namespace
 
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s) {
-    const dim3 grid((a.B + 63) / 64, a.hq);
+    if (a.tcap % 32 || a.tcap < a.S + a.B) return hipErrorInvalidValue;
+    const dim3 grid((a.B + 31) / 32, a.hq);
     if (a.hd == 128)
-        hipLaunchKernelGGL(attn_prefill_kernel<128>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(attn_prefill_kernel<128>, grid, dim3(64), 0, s, a);
     else if (a.hd == 64)
-        hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, dim3(64), 0, s, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -27,11 +27,11 @@ struct ProbeScope {
     ProbeScope(ddl_ctx* ctx, int kind, hipStream_t stream) : c(ctx), s(stream) {
         if (c->probe_kind == kind && c->probe_count < c->probe_max) {
             slot = c->probe_count++;
-            hipEventRecord(c->probe_events[2 * slot], s);
+            (void)hipEventRecord(c->probe_events[2 * slot], s);
         }
     }
     ~ProbeScope() {
-        if (slot >= 0) hipEventRecord(c->probe_events[2 * slot + 1], s);
+        if (slot >= 0) (void)hipEventRecord(c->probe_events[2 * slot + 1], s);
     }
 };
 
@@ -84,31 +84,56 @@ struct GemmArgs {
     float* C; int ldc;          // EPI_F32, EPI_RESID output
     const float* R; int ldr;    // EPI_RESID residual input (may alias C)
     f16* H; int ldh;            // EPI_SWIGLU output [M][N/2]
+    int splits;                 // split-K factor (0 or 1: none); split z > 0 stores
+    float* P;                   // raw partials at P + (z-1)*M*N, [M][N]
 };
+enum { GEMM_CFG_128x128 = 0, GEMM_CFG_256x128 = 1 };
+struct GemmPlan {
+    int cfg;
+    int splits;
+};
+GemmPlan gemm_plan(int M, int N, int K, int epi);
+// Launches with the plan's tile and split-K factor (a.splits is ignored);
+// with splits > 1, a.P must hold (splits-1)*M*N floats.
 hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s);
 bool gemm_shape_ok(int M, int N, int K, int epi);
 
-hipError_t launch_rmsnorm_f16(const float* x, const float* g, f16* h, int rows, int d,
-                              float eps, hipStream_t s);
+// h = rms_norm(x + P_0 + ... + P_{np-1}) * g as fp16; with np > 0 the completed
+// row is also written to xout (which may alias x).  Partial z is at P + z*rows*d.
+hipError_t launch_rmsnorm_f16(const float* x, const float* P, int np, float* xout, const float* g,
+                              f16* h, int rows, int d, float eps, hipStream_t s);
+hipError_t launch_add_partials(float* x, const float* P, int np, size_t n, hipStream_t s);
 
 hipError_t launch_rope_table(float2* tab, int batch, int start_pos, int half, int rot_dim,
                              double theta, hipStream_t s);
 
+// Staged fp16 K/V of one layer for the attention kernel, tcap rows per KV
+// head (a multiple of 32, at least S + 32*(ceil(B/32)+1)):
+//   k16  [hkv][tcap][hd]   key j = cached row j (j < S) or new row j - S
+//   vt16 [hkv][hd][tcap]   the same values transposed
 struct QkvPostArgs {
-    const float* qkv; int nqkv;         // [B][nqkv] GEMM output
+    float* qkv; int nqkv;               // [B][nqkv] GEMM output (split 0); gate completed in place
+    const float* P; int np; size_t pstride;   // split-K partials of the GEMM
     const float* bias;                  // [nqkv] or null
     const float* q_norm; const float* k_norm;   // [hd] or null
     const float2* rope;                 // [B][hd/2] or null
-    int B, hq, hkv, hd; float eps;
+    int B, S, hq, hkv, hd, gated; float eps;
     f16* q16;                           // [B][hq*hd]
     float* k_rows; float* v_rows;       // [B][hkv*hd]
+    f16* k16; f16* vt16; int tcap;
 };
 hipError_t launch_qkv_post(const QkvPostArgs& a, hipStream_t s);
 
+struct StagePrefixArgs {
+    const float* pk; const float* pv;   // [S][hkv*hd]
+    int S, hkv, hd;
+    f16* k16; f16* vt16; int tcap;
+};
+hipError_t launch_stage_prefix(const StagePrefixArgs& a, hipStream_t s);
+
 struct AttnPrefillArgs {
     const f16* q16;                      // [B][hq*hd]
-    const float* pk; const float* pv;    // [S][hkv*hd] cached rows (null when S == 0)
-    const float* nk; const float* nv;    // [B][hkv*hd] new rows
+    const f16* k16; const f16* vt16; int tcap;   // staged keys/values (QkvPostArgs)
     const float* gate; int gate_ld;      // gate (B rows, stride gate_ld) or null
     f16* o16;                            // [B][hq*hd]
     int B, S, hq, hkv, hd;

@@ -13,8 +13,12 @@
 
 namespace {
 
-// One 256-thread block per row; d % 4 == 0.
+// One 256-thread block per row; d % 4 == 0.  With np > 0 the row is first
+// completed from split-K partials (x + P_0 + ... + P_{np-1}, in that order)
+// and the completed row is written back to xout.
 __global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const float* __restrict__ x,
+                                                          const float* __restrict__ P, int np,
+                                                          size_t pstride, float* xout,
                                                           const float* __restrict__ g,
                                                           f16* __restrict__ h, int d, float eps) {
     __shared__ float red[4];
@@ -24,16 +28,35 @@ __global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const float* __restric
     const int n4 = d >> 2;
     float ss = 0.f;
     for (int i = threadIdx.x; i < n4; i += 256) {
-        const float4 v = xr[i];
+        float4 v = xr[i];
+        for (int z = 0; z < np; ++z) {
+            const float4 q = reinterpret_cast<const float4*>(P + z * pstride + row * d)[i];
+            v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
+        }
+        if (np) reinterpret_cast<float4*>(xout + row * d)[i] = v;
         ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
     }
-    ss = block_sum_256(ss, red);
+    ss = block_sum_256(ss, red);   // (its barriers also order the xout writes before the reads)
     const float r = 1.0f / sqrtf(ss / (float)d + eps);
+    const float4* src = np ? reinterpret_cast<const float4*>(xout + row * d) : xr;
     half4* hr = reinterpret_cast<half4*>(h + row * d);
     for (int i = threadIdx.x; i < n4; i += 256) {
-        const float4 v = xr[i], w = gr[i];
+        const float4 v = src[i], w = gr[i];
         hr[i] = half4{(f16)(v.x * r * w.x), (f16)(v.y * r * w.y), (f16)(v.z * r * w.z),
                       (f16)(v.w * r * w.w)};
+    }
+}
+
+// x += P_0 + ... + P_{np-1} (the last layer's split-K partials).
+__global__ __launch_bounds__(256) void add_partials_kernel(float* x, const float* __restrict__ P,
+                                                           int np, size_t n4) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+        float4 v = reinterpret_cast<float4*>(x)[i];
+        for (int z = 0; z < np; ++z) {
+            const float4 q = reinterpret_cast<const float4*>(P + z * n4 * 4)[i];
+            v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
+        }
+        reinterpret_cast<float4*>(x)[i] = v;
     }
 }
 
@@ -49,57 +72,149 @@ __global__ void rope_table_kernel(float2* tab, int batch, int start_pos, int hal
     tab[idx] = make_float2((float)cos(ang), (float)sin(ang));
 }
 
-// One wave per (token, head slot): slots [0, hq) are q heads, [hq, hq+hkv)
-// k heads, [hq+hkv, hq+2*hkv) v heads.  Lane l holds the Neox pair
-// (l, l + hd/2); for hd = 64 lanes 32..63 only take part in the reductions.
+// One 256-thread block per (block of 32 tokens, head slot).  Slots: [0, hq)
+// q heads, [hq, hq+hkv) k heads, [hq+hkv, hq+2hkv) v heads, then (gated
+// layers) hq gate heads.  Thread t takes token t/8 and head elements
+// [(t%8)*HD/8, +HD/8); the Neox partner of element e (e < HD/2) lives in
+// thread t^4.  Each value is first completed from the split-K partials.
+// q goes to q16 (fp16), k to the K rows (fp32) and to K16[g][S+b] (fp16),
+// v to the V rows (fp32) and, transposed through LDS, to Vt16[g][e][S+b];
+// the gate is written back in place.  Block index nblk (one past the last
+// token block) zero-fills K16/Vt16 rows [S+32*nblk, S+32*nblk+32), so every
+// 32-key tile the attention reads is finite.
+template <int HD>
 __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs p) {
-    const int lane = threadIdx.x & 63;
-    const int slots = p.hq + 2 * p.hkv;
-    const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (item >= p.B * slots) return;
-    const int b = item / slots, slot = item - b * slots;
-    const int half = p.hd >> 1;
-    const bool active = lane < half;
-    const int col0 = slot * p.hd;     // q, k, v slots are contiguous columns
-    const float* src = p.qkv + (size_t)b * p.nqkv + col0;
-    float x0 = 0.f, x1 = 0.f;
-    if (active) {
-        x0 = src[lane];
-        x1 = src[lane + half];
-        if (p.bias) {
-            x0 += p.bias[col0 + lane];
-            x1 += p.bias[col0 + lane + half];
+    constexpr int EPT = HD / 8;          // elements per thread
+    __shared__ f16 vt[HD][33];
+    const int tid = threadIdx.x, tl = tid >> 3, part = tid & 7;
+    const int blk = blockIdx.x, slot = blockIdx.y;
+    const int nblk = (p.B + 31) / 32;
+    const int b = blk * 32 + tl;
+    const bool is_q = slot < p.hq, is_k = !is_q && slot < p.hq + p.hkv;
+    const bool is_v = !is_q && !is_k && slot < p.hq + 2 * p.hkv;
+    const int g = is_k ? slot - p.hq : (is_v ? slot - p.hq - p.hkv : 0);
+    const int e0 = part * EPT;
+    const bool valid = blk < nblk && b < p.B;
+    if (blk == nblk && !is_k && !is_v) return;
+
+    float x[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) x[i] = 0.f;
+    const int col0 = slot * HD + e0;     // q, k, v, gate slots are contiguous columns
+    if (valid) {
+        const float* src = p.qkv + (size_t)b * p.nqkv + col0;
+        const float* psrc = p.P + (size_t)b * p.nqkv + col0;   // partial z at psrc + z*pstride
+#pragma unroll
+        for (int i = 0; i < EPT; i += 4) {
+            float4 v = *reinterpret_cast<const float4*>(src + i);
+            for (int z = 0; z < p.np; ++z) {
+                const float4 q = *reinterpret_cast<const float4*>(psrc + z * p.pstride + i);
+                v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
+            }
+            x[i] = v.x; x[i + 1] = v.y; x[i + 2] = v.z; x[i + 3] = v.w;
+        }
+        if (p.bias && slot < p.hq + 2 * p.hkv) {
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) x[i] += p.bias[col0 + i];
         }
     }
-    const bool is_q = slot < p.hq, is_k = !is_q && slot < p.hq + p.hkv;
+    if (slot >= p.hq + 2 * p.hkv) {      // gate: completed value back in place
+        if (valid && p.np) {
+            float* dst = p.qkv + (size_t)b * p.nqkv + col0;
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) dst[i] = x[i];
+        }
+        return;
+    }
     if (is_q || is_k) {
         const float* gn = is_q ? p.q_norm : p.k_norm;
         if (gn) {
-            const float ss = wave_sum(x0 * x0 + x1 * x1);
-            const float r = 1.0f / sqrtf(ss / (float)p.hd + p.eps);
-            if (active) {
-                x0 = x0 * r * gn[lane];
-                x1 = x1 * r * gn[lane + half];
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) ss += x[i] * x[i];
+            ss += __shfl_xor(ss, 1, 64);
+            ss += __shfl_xor(ss, 2, 64);
+            ss += __shfl_xor(ss, 4, 64);
+            const float r = 1.0f / sqrtf(ss / (float)HD + p.eps);
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) x[i] = x[i] * r * gn[e0 + i];
+        }
+        if (p.rope) {
+            const bool first = part < 4;          // holds the a of the pairs (a, b)
+            const int ebase = (first ? e0 : e0 - HD / 2);
+            const float2* cs = p.rope + (size_t)(valid ? b : 0) * (HD / 2) + ebase;
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) {
+                const float other = __shfl_xor(x[i], 4, 64);
+                const float2 c = cs[i];
+                x[i] = first ? x[i] * c.x - other * c.y : other * c.y + x[i] * c.x;
             }
         }
-        if (p.rope && active) {
-            const float2 cs = p.rope[(size_t)b * half + lane];
-            const float y0 = x0 * cs.x - x1 * cs.y;
-            const float y1 = x0 * cs.y + x1 * cs.x;
-            x0 = y0;
-            x1 = y1;
-        }
     }
-    if (!active) return;
     if (is_q) {
-        f16* dst = p.q16 + (size_t)b * p.hq * p.hd + slot * p.hd;
-        dst[lane] = (f16)x0;
-        dst[lane + half] = (f16)x1;
-    } else {
-        const int g = is_k ? slot - p.hq : slot - p.hq - p.hkv;
-        float* dst = (is_k ? p.k_rows : p.v_rows) + (size_t)b * p.hkv * p.hd + g * p.hd;
-        dst[lane] = x0;
-        dst[lane + half] = x1;
+        if (valid) {
+            f16* dst = p.q16 + (size_t)b * p.hq * HD + slot * HD + e0;
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) dst[i] = (f16)x[i];
+        }
+        return;
+    }
+    const size_t key = (size_t)p.S + b;            // row in the staged K/V
+    if (is_k) {
+        if (valid) {
+            float* dst = p.k_rows + (size_t)b * p.hkv * HD + g * HD + e0;
+#pragma unroll
+            for (int i = 0; i < EPT; i += 4)
+                *reinterpret_cast<float4*>(dst + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
+        }
+        f16* kd = p.k16 + ((size_t)g * p.tcap + key) * HD + e0;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) kd[i] = (f16)x[i];     // zeros past B
+        return;
+    }
+    // v
+    if (valid) {
+        float* dst = p.v_rows + (size_t)b * p.hkv * HD + g * HD + e0;
+#pragma unroll
+        for (int i = 0; i < EPT; i += 4)
+            *reinterpret_cast<float4*>(dst + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
+    }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) vt[e0 + i][tl] = (f16)x[i];
+    __syncthreads();
+    // row e of Vt16 gets this block's 32 keys
+    for (int idx = tid; idx < HD * 32; idx += 256) {
+        const int e = idx >> 5, t = idx & 31;
+        p.vt16[((size_t)g * HD + e) * p.tcap + p.S + blk * 32 + t] = vt[e][t];
+    }
+}
+
+// Cached rows [0, S) of one layer into the staged fp16 layouts: K16[g][j]
+// and Vt16[g][e][j].  One block per (32 rows, KV head).
+template <int HD>
+__global__ __launch_bounds__(256) void stage_prefix_kernel(StagePrefixArgs p) {
+    __shared__ f16 vt[HD][33];
+    const int blk = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+    const int kvw = p.hkv * HD;
+    for (int idx = tid; idx < 32 * HD / 4; idx += 256) {
+        const int t = idx / (HD / 4), e = (idx % (HD / 4)) * 4;
+        const int j = blk * 32 + t;
+        float4 k = make_float4(0.f, 0.f, 0.f, 0.f), v = k;
+        if (j < p.S) {
+            k = *reinterpret_cast<const float4*>(p.pk + (size_t)j * kvw + g * HD + e);
+            v = *reinterpret_cast<const float4*>(p.pv + (size_t)j * kvw + g * HD + e);
+            *reinterpret_cast<half4*>(p.k16 + ((size_t)g * p.tcap + j) * HD + e) =
+                half4{(f16)k.x, (f16)k.y, (f16)k.z, (f16)k.w};
+        }
+        vt[e][t] = (f16)v.x;
+        vt[e + 1][t] = (f16)v.y;
+        vt[e + 2][t] = (f16)v.z;
+        vt[e + 3][t] = (f16)v.w;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < HD * 32; idx += 256) {
+        const int e = idx >> 5, t = idx & 31, j = blk * 32 + t;
+        if (j < p.S) p.vt16[((size_t)g * HD + e) * p.tcap + j] = vt[e][t];
     }
 }
 
@@ -156,9 +271,16 @@ int grid_for(size_t n) {
 
 }  // namespace
 
-hipError_t launch_rmsnorm_f16(const float* x, const float* g, f16* h, int rows, int d, float eps,
-                              hipStream_t s) {
-    hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3(rows), dim3(256), 0, s, x, g, h, d, eps);
+hipError_t launch_rmsnorm_f16(const float* x, const float* P, int np, float* xout, const float* g,
+                              f16* h, int rows, int d, float eps, hipStream_t s) {
+    hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3(rows), dim3(256), 0, s, x, P, np,
+                       (size_t)rows * d, xout, g, h, d, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_add_partials(float* x, const float* P, int np, size_t n, hipStream_t s) {
+    const size_t n4 = n / 4;
+    hipLaunchKernelGGL(add_partials_kernel, dim3(grid_for(n4)), dim3(256), 0, s, x, P, np, n4);
     return hipGetLastError();
 }
 
@@ -171,8 +293,25 @@ hipError_t launch_rope_table(float2* tab, int batch, int start_pos, int half, in
 }
 
 hipError_t launch_qkv_post(const QkvPostArgs& a, hipStream_t s) {
-    const int items = a.B * (a.hq + 2 * a.hkv);
-    hipLaunchKernelGGL(qkv_post_kernel, dim3((items + 3) / 4), dim3(256), 0, s, a);
+    const dim3 grid((a.B + 31) / 32 + 1, (a.gated ? 2 : 1) * a.hq + 2 * a.hkv);
+    if (a.hd == 128)
+        hipLaunchKernelGGL(qkv_post_kernel<128>, grid, dim3(256), 0, s, a);
+    else if (a.hd == 64)
+        hipLaunchKernelGGL(qkv_post_kernel<64>, grid, dim3(256), 0, s, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_stage_prefix(const StagePrefixArgs& a, hipStream_t s) {
+    if (a.S <= 0) return hipSuccess;
+    const dim3 grid((a.S + 31) / 32, a.hkv);
+    if (a.hd == 128)
+        hipLaunchKernelGGL(stage_prefix_kernel<128>, grid, dim3(256), 0, s, a);
+    else if (a.hd == 64)
+        hipLaunchKernelGGL(stage_prefix_kernel<64>, grid, dim3(256), 0, s, a);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

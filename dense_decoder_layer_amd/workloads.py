@@ -37,7 +37,7 @@ class DeviceStack:
                 raise ValueError("layer declined by ddl_layer_pack")
             self.layers.append(layer)
 
-    def buffers(self, batch: int):
+    def buffers(self, batch: int, start_pos: int = 0):
         kvw = self.cfg.n_kv_heads * self.cfg.head_dim
         n = len(self.layers)
         f32 = dict(dtype=torch.float32, device=self.device)
@@ -45,8 +45,8 @@ class DeviceStack:
             "hidden_out": torch.empty(batch, self.cfg.d_model, **f32),
             "k_rows": [torch.empty(batch, kvw, **f32) for _ in range(n)],
             "v_rows": [torch.empty(batch, kvw, **f32) for _ in range(n)],
-            "workspace": torch.empty(ddl_workspace_bytes(self.layers, batch), dtype=torch.uint8,
-                                     device=self.device),
+            "workspace": torch.empty(ddl_workspace_bytes(self.layers, batch, start_pos),
+                                     dtype=torch.uint8, device=self.device),
         }
 
     def run(self, hidden: torch.Tensor, start_pos: int,

@@ -140,9 +140,13 @@ int ddl_layer_pack(ddl_ctx* ctx, const ddl_layer_desc* desc,
                    void* stream, ddl_layer** out);
 void ddl_layer_destroy(ddl_layer* layer);
 
-/* Workspace bytes a prefill of up to max_batch tokens over `n` layers needs
- * (the start position does not change it). */
-size_t ddl_workspace_bytes(const ddl_layer* const* layers, int n, int max_batch);
+/* Workspace bytes a prefill of up to max_batch tokens at a start position of
+ * up to max_start_pos needs over `n` layers (0 on bad arguments).  The
+ * workspace holds the per-layer intermediates, the layer's keys and values
+ * staged as fp16, and split-K partial sums; its contents do not outlive a
+ * call. */
+size_t ddl_workspace_bytes(const ddl_layer* const* layers, int n, int max_batch,
+                           int max_start_pos);
 
 /* Batched prefill of the longest servable run of consecutive layers
  * ([P1] module doc and try_cuda_prefill_dense_stack).

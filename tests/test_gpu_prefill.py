@@ -45,7 +45,7 @@ def gpu_run(ddl, cfg, inp, min_batch=1, hidden=None):
     from dense_decoder_layer_amd.workloads import DeviceStack
     ctx = ddl.ddl_ctx_create(min_batch=min_batch)
     stack = DeviceStack(ctx, cfg, inp.layers)
-    bufs = stack.buffers(cfg.batch)
+    bufs = stack.buffers(cfg.batch, cfg.start_pos)
     h = torch.from_numpy(inp.hidden if hidden is None else hidden).cuda()
     pk = [torch.from_numpy(a).cuda() for a in inp.prefix_k] if cfg.start_pos else None
     pv = [torch.from_numpy(a).cuda() for a in inp.prefix_v] if cfg.start_pos else None
