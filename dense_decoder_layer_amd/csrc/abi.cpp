@@ -86,9 +86,8 @@ void blob_layout(const ddl_layer_desc* d, BlobLayout* L) {
 
 // Per-call scratch in the caller's workspace.
 struct WsLayout {
-    size_t rope, h, qkv, q16, o16, x1, a16, k16, vt16, part, total;
+    size_t rope, h, qkv, q16, o16, x1, a16, k16, vt16, total;
     int tcap;
-    int sq, so, sd;    // split-K factors of the qkv, wo and down projections
 };
 
 int staged_rows(int B, int S) {
@@ -105,12 +104,6 @@ WsLayout ws_layout(const ddl_layer* L, int B, int S) {
         return at;
     };
     w.tcap = staged_rows(B, S);
-    w.sq = gemm_plan(B, L->nqkv, L->d, EPI_F32).splits;
-    w.so = gemm_plan(B, L->d, L->hq * L->hd, EPI_RESID).splits;
-    w.sd = gemm_plan(B, L->d, L->f, EPI_RESID).splits;
-    size_t part = (size_t)(w.sq - 1) * L->nqkv;
-    if ((size_t)(w.so - 1) * L->d > part) part = (size_t)(w.so - 1) * L->d;
-    if ((size_t)(w.sd - 1) * L->d > part) part = (size_t)(w.sd - 1) * L->d;
     w.rope = take((size_t)B * (L->hd / 2) * sizeof(float2));
     w.h = take((size_t)B * L->d * 2);
     w.qkv = take((size_t)B * L->nqkv * 4);
@@ -120,7 +113,6 @@ WsLayout ws_layout(const ddl_layer* L, int B, int S) {
     w.a16 = take((size_t)B * L->f * 2);
     w.k16 = take((size_t)L->hkv * w.tcap * L->hd * 2);
     w.vt16 = take((size_t)L->hkv * w.tcap * L->hd * 2);
-    w.part = take(part * B * 4);
     w.total = o;
     return w;
 }
@@ -319,11 +311,8 @@ size_t ddl_workspace_bytes(const ddl_layer* const* layers, int n, int max_batch,
     size_t need = 0;
     for (int i = 0; i < n; ++i) {
         if (!layers[i]) return 0;
-        // the split-K plan depends on the batch, so every batch size counts
-        for (int b = 1; b <= max_batch; ++b) {
-            const size_t t = ws_layout(layers[i], b, max_start_pos).total;
-            if (t > need) need = t;
-        }
+        const size_t t = ws_layout(layers[i], max_batch, max_start_pos).total;
+        if (t > need) need = t;
     }
     return need;
 }
@@ -375,19 +364,17 @@ int ddl_prefill_dense_stack(ddl_ctx* ctx, const float* hidden, const ddl_layer* 
     f16* a16 = reinterpret_cast<f16*>(ws + W.a16);
     f16* k16 = reinterpret_cast<f16*>(ws + W.k16);
     f16* vt16 = reinterpret_cast<f16*>(ws + W.vt16);
-    float* part = reinterpret_cast<float*>(ws + W.part);
     const int d = L0->d, hq = L0->hq, hkv = L0->hkv, hd = L0->hd, f = L0->f, nqkv = L0->nqkv;
 
     hipError_t e = hipSuccess;
     if (L0->rope_on) e = launch_rope_table(rope, batch, start_pos, hd / 2, hd, L0->theta, s);
-    int pending = 0;   // down-projection partials of the previous layer still in `part`
     for (int l = 0; l < run && !e; ++l) {
         const ddl_layer* L = layers[l];
-        float* x = l == 0 ? const_cast<float*>(hidden) : hidden_out;
+        const float* x = l == 0 ? hidden : hidden_out;
         // attention branch: x1 = x + wo . attn(rope(qkv(rms_norm(x))))
         {
             ProbeScope p(ctx, DDL_K_RMSNORM, s);
-            e = launch_rmsnorm_f16(x, part, pending, hidden_out, L->g_attn, h, batch, d, L->eps, s);
+            e = launch_rmsnorm_f16(x, L->g_attn, h, batch, d, L->eps, s);
         }
         if (!e && start_pos > 0) {
             StagePrefixArgs sp{};
@@ -401,14 +388,13 @@ int ddl_prefill_dense_stack(ddl_ctx* ctx, const float* hidden, const ddl_layer* 
             g.A = h; g.lda = d; g.W = L->wqkv; g.ldw = d;
             g.M = batch; g.N = nqkv; g.K = d;
             g.inv_scale = &L->hdr->inv_scale[MAT_QKV];
-            g.C = qkv; g.ldc = nqkv; g.P = part;
+            g.C = qkv; g.ldc = nqkv;
             ProbeScope p(ctx, DDL_K_GEMM_QKV, s);
             e = launch_gemm(g, EPI_F32, s);
         }
         if (!e) {
             QkvPostArgs q{};
             q.qkv = qkv; q.nqkv = nqkv;
-            q.P = part; q.np = W.sq - 1; q.pstride = (size_t)batch * nqkv;
             q.bias = L->bqkv; q.q_norm = L->q_norm; q.k_norm = L->k_norm;
             q.rope = L->rope_on ? rope : nullptr;
             q.B = batch; q.S = start_pos; q.hq = hq; q.hkv = hkv; q.hd = hd; q.gated = L->gated;
@@ -434,14 +420,14 @@ int ddl_prefill_dense_stack(ddl_ctx* ctx, const float* hidden, const ddl_layer* 
             g.A = o16; g.lda = hq * hd; g.W = L->wo; g.ldw = hq * hd;
             g.M = batch; g.N = d; g.K = hq * hd;
             g.inv_scale = &L->hdr->inv_scale[MAT_O];
-            g.C = x1; g.ldc = d; g.R = x; g.ldr = d; g.P = part;
+            g.C = x1; g.ldc = d; g.R = x; g.ldr = d;
             ProbeScope p(ctx, DDL_K_GEMM_WO, s);
             e = launch_gemm(g, EPI_RESID, s);
         }
         // FFN branch: out = x1 + down(silu(gate(h2)) * up(h2)), h2 = rms_norm(x1)
         if (!e) {
             ProbeScope p(ctx, DDL_K_RMSNORM, s);
-            e = launch_rmsnorm_f16(x1, part, W.so - 1, x1, L->g_ffn, h, batch, d, L->eps, s);
+            e = launch_rmsnorm_f16(x1, L->g_ffn, h, batch, d, L->eps, s);
         }
         if (!e) {
             GemmArgs g{};
@@ -457,13 +443,11 @@ int ddl_prefill_dense_stack(ddl_ctx* ctx, const float* hidden, const ddl_layer* 
             g.A = a16; g.lda = f; g.W = L->wd; g.ldw = f;
             g.M = batch; g.N = d; g.K = f;
             g.inv_scale = &L->hdr->inv_scale[MAT_D];
-            g.C = hidden_out; g.ldc = d; g.R = x1; g.ldr = d; g.P = part;
+            g.C = hidden_out; g.ldc = d; g.R = x1; g.ldr = d;
             ProbeScope p(ctx, DDL_K_GEMM_DOWN, s);
             e = launch_gemm(g, EPI_RESID, s);
         }
-        pending = W.sd - 1;
     }
-    if (!e && pending > 0) e = launch_add_partials(hidden_out, part, pending, (size_t)batch * d, s);
     if (e) return fail(DDL_ERR_DEVICE, std::string("prefill launch: ") + hipGetErrorString(e));
     g_err.clear();
     return run;

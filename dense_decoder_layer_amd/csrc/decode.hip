@@ -187,79 +187,74 @@ __global__ __launch_bounds__(HD) void decode_attn_combine_kernel(DecodeAttnArgs 
     p.o[(size_t)h * HD + d] = r;
 }
 
-// y = W x (fp16 weights times inv_scale, fp32 x) with fused epilogues.
-// A workgroup stages x (optionally RMS-normed) in LDS; each wave owns
-// GV_ROWS rows at a time, its lanes walk 16-byte weight chunks c = lane,
-// lane + 64, ... and the row sums are reduced across the wave.
-constexpr int GV_ROWS = 4;      // rows per wave per pass
+// y = W x (fp16 weights times inv_scale, fp32 x) with fused epilogues; W in
+// MFMA-fragment order.  One 512-thread workgroup per 32-row block: x (RMS-
+// normed first when norm_g is set) is staged in LDS, the eight waves split
+// the 16-column blocks of K round-robin, and lane l accumulates row l % 32
+// over columns 16kb + 8*(l/32) .. +7 of each 1 KB fragment block it loads
+// (one fully coalesced load per block).  The halves of a row meet with one
+// shuffle, the waves in LDS, in a fixed order.
+constexpr int GV_WAVES = 8;
 constexpr int GV_MAXK = 15872;  // largest K the LDS stage holds (62 KB of dynamic LDS)
 
 template <int EPI>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs p) {
+__global__ __launch_bounds__(GV_WAVES * 64) void gemv_kernel(GemvArgs p) {
     extern __shared__ float xs[];   // [K]
-    __shared__ float red[4];
+    __shared__ float red[GV_WAVES][32];
+    __shared__ float wsum[GV_WAVES];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int i = tid; i < p.K; i += 256) xs[i] = p.x[i];
+    for (int i = tid; i < p.K; i += GV_WAVES * 64) xs[i] = p.x[i];
     if (p.norm_g) {
         float ss = 0.f;
-        for (int i = tid; i < p.K; i += 256) ss += xs[i] * xs[i];
+        for (int i = tid; i < p.K; i += GV_WAVES * 64) ss += p.x[i] * p.x[i];
+        ss = wave_sum(ss);
+        if (lane == 0) wsum[wave] = ss;
         __syncthreads();
-        ss = block_sum_256(ss, red);
-        const float r = 1.0f / sqrtf(ss / (float)p.K + p.eps);
-        for (int i = tid; i < p.K; i += 256) xs[i] = xs[i] * r * p.norm_g[i];
+        float t = 0.f;
+#pragma unroll
+        for (int w = 0; w < GV_WAVES; ++w) t += wsum[w];
+        const float r = 1.0f / sqrtf(t / (float)p.K + p.eps);
+        for (int i = tid; i < p.K; i += GV_WAVES * 64) xs[i] = xs[i] * r * p.norm_g[i];
     }
     __syncthreads();
-    const float sc = *p.inv_scale;
-    const int nchunks = p.K >> 3;
-    // output rows of this wave
-    const int out0 = (blockIdx.x * 4 + wave) * (EPI == GV_SWIGLU ? GV_ROWS / 2 : GV_ROWS);
-    int wrow[GV_ROWS];
-    bool ok[GV_ROWS];
+    const int nb = blockIdx.x;
+    const int kblocks = p.K >> 4;
+    const f16* wb = p.W + (size_t)nb * kblocks * 512 + lane * 8;
+    const float* xl = xs + 8 * (lane >> 5);
+    float acc = 0.f;
+    int kb = wave;
+    for (; kb + 3 * GV_WAVES < kblocks; kb += 4 * GV_WAVES) {
+        half8 w[4];
 #pragma unroll
-    for (int r = 0; r < GV_ROWS; ++r) {
-        if constexpr (EPI == GV_SWIGLU) {
-            const int f = out0 + (r >> 1);
-            ok[r] = f < p.N;
-            wrow[r] = (f >> 4) * 32 + (r & 1) * 16 + (f & 15);
-        } else {
-            ok[r] = out0 + r < p.N;
-            wrow[r] = out0 + r;
-        }
-        if (!ok[r]) wrow[r] = 0;
-    }
-    float acc[GV_ROWS];
+        for (int u = 0; u < 4; ++u) w[u] = *reinterpret_cast<const half8*>(wb + (size_t)(kb + u * GV_WAVES) * 512);
 #pragma unroll
-    for (int r = 0; r < GV_ROWS; ++r) acc[r] = 0.f;
-    for (int c = lane; c < nchunks; c += 64) {
-        half8 w[GV_ROWS];
+        for (int u = 0; u < 4; ++u) {
+            const float* xv = xl + (kb + u * GV_WAVES) * 16;
 #pragma unroll
-        for (int r = 0; r < GV_ROWS; ++r)
-            w[r] = *reinterpret_cast<const half8*>(p.W + (size_t)wrow[r] * p.K + c * 8);
-        const float4 xa = *reinterpret_cast<const float4*>(&xs[c * 8]);
-        const float4 xb = *reinterpret_cast<const float4*>(&xs[c * 8 + 4]);
-#pragma unroll
-        for (int r = 0; r < GV_ROWS; ++r) {
-            acc[r] += (float)w[r][0] * xa.x + (float)w[r][1] * xa.y + (float)w[r][2] * xa.z +
-                      (float)w[r][3] * xa.w + (float)w[r][4] * xb.x + (float)w[r][5] * xb.y +
-                      (float)w[r][6] * xb.z + (float)w[r][7] * xb.w;
+            for (int j = 0; j < 8; ++j) acc += (float)w[u][j] * xv[j];
         }
     }
+    for (; kb < kblocks; kb += GV_WAVES) {
+        const half8 w = *reinterpret_cast<const half8*>(wb + (size_t)kb * 512);
+        const float* xv = xl + kb * 16;
 #pragma unroll
-    for (int r = 0; r < GV_ROWS; ++r) acc[r] = wave_sum(acc[r]) * sc;
-    if (lane != 0) return;
+        for (int j = 0; j < 8; ++j) acc += (float)w[j] * xv[j];
+    }
+    acc += __shfl_xor(acc, 32, 64);
+    if (lane < 32) red[wave][lane] = acc;
+    __syncthreads();
+    if (tid >= 32) return;
+    float y = 0.f;
+#pragma unroll
+    for (int w = 0; w < GV_WAVES; ++w) y += red[w][tid];
+    y *= *p.inv_scale;
     if constexpr (EPI == GV_SWIGLU) {
-#pragma unroll
-        for (int r = 0; r < GV_ROWS; r += 2) {
-            const int f = out0 + (r >> 1);
-            if (f < p.N) {
-                const float gt = acc[r], up = acc[r + 1];
-                p.y[f] = gt / (1.0f + expf(-gt)) * up;
-            }
-        }
+        // rows 32nb + t: t < 16 gate, t >= 16 up, of output 16nb + t % 16
+        const float other = __shfl_xor(y, 16, 64);
+        if (tid < 16) p.y[nb * 16 + tid] = y / (1.0f + expf(-y)) * other;
     } else {
-#pragma unroll
-        for (int r = 0; r < GV_ROWS; ++r)
-            if (ok[r]) p.y[out0 + r] = p.r[out0 + r] + acc[r];
+        const int row = nb * 32 + tid;
+        p.y[row] = p.r[row] + y;
     }
 }
 
@@ -305,15 +300,17 @@ hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-bool gemv_shape_ok(int K) { return K > 0 && K % 8 == 0 && K <= GV_MAXK; }
+bool gemv_shape_ok(int K) { return K > 0 && K % 16 == 0 && K <= GV_MAXK; }
 
 hipError_t launch_gemv(const GemvArgs& a, int epi, hipStream_t s) {
     if (!gemv_shape_ok(a.K)) return hipErrorInvalidValue;
-    const int per_block = 4 * (epi == GV_SWIGLU ? GV_ROWS / 2 : GV_ROWS);
-    const dim3 grid((a.N + per_block - 1) / per_block);
+    // GV_SWIGLU: N outputs from 2N packed rows; GV_RESID: N rows
+    const int rows = epi == GV_SWIGLU ? 2 * a.N : a.N;
+    if (rows % 32) return hipErrorInvalidValue;
+    const dim3 grid(rows / 32);
     if (epi == GV_SWIGLU)
-        hipLaunchKernelGGL(gemv_kernel<GV_SWIGLU>, grid, dim3(256), a.K * sizeof(float), s, a);
+        hipLaunchKernelGGL(gemv_kernel<GV_SWIGLU>, grid, dim3(GV_WAVES * 64), a.K * sizeof(float), s, a);
     else
-        hipLaunchKernelGGL(gemv_kernel<GV_RESID>, grid, dim3(256), a.K * sizeof(float), s, a);
+        hipLaunchKernelGGL(gemv_kernel<GV_RESID>, grid, dim3(GV_WAVES * 64), a.K * sizeof(float), s, a);
     return hipGetLastError();
 }

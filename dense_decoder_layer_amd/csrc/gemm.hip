@@ -1,9 +1,8 @@
 // fp16 MFMA GEMM with fused epilogues for the layer's projections:
 //   C[M][N] = A[M][K] * W[N][K]^T * inv_scale
 // A holds token-major activations (normed rows, attention output or SwiGLU
-// output, rounded to fp16); W holds a packed weight matrix [out][in] whose
-// fp16 values are the layer's weights times 2^shift (inv_scale undoes it).
-// Both operands are K-contiguous, so A and W fragments are read alike.
+// output, rounded to fp16); W is a packed weight matrix whose fp16 values are
+// the layer's weights times 2^shift (inv_scale undoes it).
 //
 // Epilogues (the steps between the matmuls of a layer, fused into the
 // matmul that produces their input):
@@ -12,65 +11,77 @@
 //   EPI_SWIGLU  W rows are gate/up interleaved in 16-row blocks; store
 //               fp16 silu(gate) * up into H[M][N/2]
 //
-// Tiling (gfx950): a workgroup of WGM x WGN waves computes a BM x BN tile;
-// each wave owns a (BM/WGM) x (BN/WGN) block of v_mfma_f32_32x32x16_f16
-// tiles.  K advances 64 at a time through an NS-stage ring in LDS that is
-// filled by global_load_lds_dwordx4 (global memory straight into LDS, no
-// VGPR staging), so NS-1 stages are in flight while one is consumed.  One
-// DMA instruction writes 1 KB = 8 LDS rows of 128 B, lane l at byte 16*l;
-// the lane fetches the 16-byte chunk (l % 8) ^ (row % 8) of its row, which
-// leaves every row XOR-swizzled so the fragment reads of 8 consecutive
-// lanes (one row each, same chunk) hit distinct banks.
+// Design (gfx950, v_mfma_f32_32x32x16_f16):
+//  * W is stored in MFMA-fragment order (see the packing kernels): the
+//    32 x 16 block (rows 32nb.., k 16kb..) is 1 KB in which lane l's B
+//    operand -- row 32nb + l%32, k 16kb + 8*(l/32) .. +7 -- sits at byte
+//    16*l.  A wave loads each weight fragment with one fully coalesced
+//    1 KB global load straight into registers; weights never touch LDS.
+//  * The activation tile (BM rows x 64 k) is shared by the workgroup's
+//    waves: its 16-byte chunks are loaded into registers NS-1 k-tiles
+//    ahead (consecutive threads take consecutive chunks of a row, so the
+//    loads coalesce) and written into a 2-slot LDS ring one step before
+//    use, chunk c of row r at position c ^ (r % 8), so the fragment reads
+//    of 8 consecutive lanes (one row each, same chunk) hit distinct banks.
+//    Every load of the kernel is an ordinary register load, so the
+//    hardware returns them in issue order and one counter tracks them.
+//  * Per k-tile: issue the loads of k-tile kt+NS-1, multiply k-tile kt,
+//    write k-tile kt+1's activations into the other LDS slot, barrier.
+//    For the K of the hot projections the k-loop is unrolled at compile
+//    time (straight-line code, so the compiler's own waits on the register
+//    loads are exact); other K run a generic loop.
+//  * Workgroups of the same weight tile are dispatched to the same XCD.
 #include "common.h"
 #include "internal.h"
+
+#include <type_traits>
+#include <utility>
 
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int K_ALIGN = 64;     // every K the library passes is a multiple of this
+constexpr int BK = 64;   // k per pipeline stage
 
 __device__ __forceinline__ floatx16 mfma32x32x16(half8 a, half8 b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// 16 bytes per lane from global memory straight into LDS: lane l writes
-// bytes [16l, 16l+16) after the wave-uniform LDS address `lds`.  The size-16
-// form exists on gfx950 only, so the host compilation pass (which checks the
-// builtin against a generic target) does not see it.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, 0);
-#endif
+// Waits for this wave's LDS writes (s_waitcnt lgkmcnt(0); gfx9 encoding:
+// vmcnt[3:0] + [15:14], expcnt[6:4], lgkmcnt[11:8], the others at maximum),
+// then the workgroup barrier; no LDS access moves across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
-// s_waitcnt with only vmcnt limited (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
-// lgkmcnt[11:8], vmcnt[5:4] at [15:14]).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+// Calls f(integral_constant<int, I>) for I = 0 .. N-1 (straight-line code).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>()), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>());
 }
 
 // Accumulator layout of a 32x32 MFMA tile: lane l holds column l % 32 of
 // rows 8*(e/4) + 4*(l/32) + e%4 for e = 0..15.
-template <int BM, int WM, int WN, int MI, int NI, int EPI>
-__device__ __forceinline__ void epilogue(const GemmArgs& p, floatx16 (&acc)[MI][NI], int m0, int n0,
-                                         int wm, int wn, int lane, int split) {
+template <int MI, int NI, int EPI>
+__device__ __forceinline__ void epilogue(const GemmArgs& p, floatx16 (&acc)[MI][NI], int row0,
+                                         int col0, int lane, bool full) {
     const float sc = *p.inv_scale;
-    const int rbase = m0 + wm * WM + 4 * (lane >> 5);
+    const int rbase = row0 + 4 * (lane >> 5);
     const int cl = lane & 31;
-    const bool full = m0 + BM <= p.M;      // no row of the tile is past M
     if constexpr (EPI == EPI_SWIGLU) {
-        // 32-column MFMA tile j holds gate block 2q (lanes 0..15 of the
-        // column range) and up block 2q+1 (lanes 16..31) for 16 outputs
+        // a 32-column tile holds gate block 2q (lanes 0..15 of the columns)
+        // and up block 2q+1 (lanes 16..31) of the same 16 outputs
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
+        for (int j = 0; j < NI; ++j) {
+            const int fcol = ((col0 + j * 32) >> 1) + (cl & 15);
 #pragma unroll
-            for (int j = 0; j < NI; ++j) {
-                const int col0 = n0 + wn * WN + j * 32;      // multiple of 32
-                const int fcol = (col0 >> 1) + (cl & 15);
+            for (int i = 0; i < MI; ++i) {
                 float a[16];
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
@@ -86,41 +97,21 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, floatx16 (&acc)[MI][
                     }
                 }
             }
-    } else if (split > 0) {
-        float* P = p.P + (size_t)(split - 1) * p.M * p.N;
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int j = 0; j < NI; ++j) {
-                const int col = n0 + wn * WN + j * 32 + cl;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
-                    if (full || row < p.M) P[(size_t)row * p.N + col] = acc[i][j][e] * sc;
-                }
-            }
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
-                const int col = n0 + wn * WN + j * 32 + cl;
+                const int col = col0 + j * 32 + cl;
                 float v[16];
 #pragma unroll
                 for (int e = 0; e < 16; ++e) v[e] = acc[i][j][e] * sc;
                 if constexpr (EPI == EPI_RESID) {
-                    if (full) {
 #pragma unroll
-                        for (int e = 0; e < 16; ++e) {
-                            const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
-                            v[e] += p.R[(size_t)row * p.ldr + col];
-                        }
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) {
-                            const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
-                            if (row < p.M) v[e] += p.R[(size_t)row * p.ldr + col];
-                        }
+                    for (int e = 0; e < 16; ++e) {
+                        const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
+                        if (full || row < p.M) v[e] += p.R[(size_t)row * p.ldr + col];
                     }
                 }
 #pragma unroll
@@ -132,67 +123,58 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, floatx16 (&acc)[MI][
     }
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int NS, int EPI>
-__global__ __launch_bounds__(WGM * WGN * 64) void gemm_f16_kernel(GemmArgs p) {
-    constexpr int NW = WGM * WGN;
-    constexpr int WM = BM / WGM, WN = BN / WGN;       // wave tile
-    constexpr int MI = WM / 32, NI = WN / 32;         // 32x32 MFMA tiles per wave
-    constexpr int CHUNKS = BK / 8;                    // 16-byte chunks per LDS row
-    constexpr int ROW_BYTES = BK * 2;
-    constexpr int RPI = 64 / CHUNKS;                  // rows per 1 KB DMA instruction
-    constexpr int A_INSTR = BM / RPI / NW, B_INSTR = BN / RPI / NW;   // DMA instructions per wave per stage
-    constexpr int STAGE_BYTES = (BM + BN) * ROW_BYTES;
-    static_assert(BK == 64 || BK == 128, "k-tile");
+// Workgroup of WGM x WGN waves, tile BM x (WN*WGN); wave tile (BM/WGM) x WN.
+// NK > 0: K/64 == NK, straight-line k-loop; NK == 0: generic loop.
+template <int BM, int WN, int WGM, int WGN, int NS, int EPI, int NK>
+__global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p) {
+    constexpr int NT = WGM * WGN * 64, BN = WN * WGN, WM = BM / WGM;
+    constexpr int MI = WM / 32, NI = WN / 32;
+    constexpr int A_CH = BM * 8 / NT;               // 16-byte activation chunks per thread per k-tile
+    constexpr int STAGE = BM * BK * 2;
     static_assert(MI >= 1 && NI >= 1, "wave tile below 32x32");
-    static_assert(A_INSTR >= 1 && B_INSTR >= 1 && A_INSTR * NW * RPI == BM && B_INSTR * NW * RPI == BN,
-                  "tile rows must split evenly into DMA blocks per wave");
-    static_assert(EPI != EPI_SWIGLU || (WN % 32) == 0, "swiglu pairs 16-column blocks");
+    static_assert(A_CH >= 1 && A_CH * NT == BM * 8, "activation chunks split evenly");
     static_assert(NS >= 2 && NS <= 4, "pipeline depth");
-    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
-
-    // Tile order: the workgroups of one weight tile (all M tiles of one N
-    // tile) are consecutive in the logical order, and the logical order is
-    // laid out XCD by XCD (dispatch sends workgroup i to XCD i % 8), so a
-    // weight tile is fetched into one XCD's L2 and reused there.
-    // Split-K: split z takes k-tiles [z*kper, (z+1)*kper); split 0 runs the
-    // epilogue, the others store raw fp32 partials that the consumer adds.
-    const int mt = (p.M + BM - 1) / BM, nt = p.N / BN;
-    const int total = mt * nt * p.splits;
+    const int mt = (p.M + BM - 1) / BM, nt = p.N / BN, total = mt * nt;
     int bid = blockIdx.x;
     if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
-    const int m0 = (bid % mt) * BM, n0 = ((bid / mt) % nt) * BN, split = bid / (mt * nt);
-    const int kper = p.K / BK / p.splits;
-    const size_t kbase = (size_t)split * kper * BK;
+    const int m0 = (bid % mt) * BM, n0 = (bid / mt) * BN;
+    const int nk = NK > 0 ? NK : p.K / BK;
 
-    // Per-lane DMA source offsets (in halves) for each of this wave's
-    // instructions; only k0 changes from stage to stage.
-    const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
-    size_t a_off[A_INSTR], b_off[B_INSTR];
+    const f16* a_src[A_CH];
+    int a_dst[A_CH];                                // half8 index in an LDS slot
 #pragma unroll
-    for (int j = 0; j < A_INSTR; ++j) {
-        const int r = (wave * A_INSTR + j) * RPI + lane / CHUNKS;
-        const int c = (lane % CHUNKS) ^ (r & 7);
-        const int row = min(m0 + r, p.M - 1);   // rows past M feed only discarded outputs
-        a_off[j] = (size_t)row * p.lda + kbase + c * 8;
+    for (int i = 0; i < A_CH; ++i) {
+        const int idx = i * NT + tid, r = idx >> 3, c = idx & 7;
+        a_src[i] = p.A + (size_t)min(m0 + r, p.M - 1) * p.lda + c * 8;   // rows past M: discarded outputs
+        a_dst[i] = r * 8 + (c ^ (r & 7));
     }
+    const f16* wfrag[NI];
 #pragma unroll
-    for (int j = 0; j < B_INSTR; ++j) {
-        const int r = (wave * B_INSTR + j) * RPI + lane / CHUNKS;
-        const int c = (lane % CHUNKS) ^ (r & 7);
-        b_off[j] = (size_t)(n0 + r) * p.ldw + kbase + c * 8;
-    }
-    auto issue = [&](int kt, int slot) {
-        const int k0 = kt * BK;
-        const uint32_t sbase = smem_base + slot * STAGE_BYTES;
+    for (int j = 0; j < NI; ++j)
+        wfrag[j] = p.W + (size_t)((n0 + wn * WN) / 32 + j) * (p.K / 16) * 512 + lane * 8;
+
+    half8 areg[NS][A_CH];
+    half8 breg[NS][NI][BK / 16];
+    auto issue = [&](int kt, auto slot_c) {
+        constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
-        for (int j = 0; j < A_INSTR; ++j)
-            dma16(p.A + a_off[j] + k0, sbase + (wave * A_INSTR + j) * 1024);
+        for (int i = 0; i < A_CH; ++i)
+            areg[slot][i] = *reinterpret_cast<const half8*>(a_src[i] + (size_t)kt * BK);
 #pragma unroll
-        for (int j = 0; j < B_INSTR; ++j)
-            dma16(p.W + b_off[j] + k0, sbase + BM * ROW_BYTES + (wave * B_INSTR + j) * 1024);
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int ks = 0; ks < BK / 16; ++ks)
+                breg[slot][j][ks] = *reinterpret_cast<const half8*>(wfrag[j] + (size_t)(kt * 4 + ks) * 512);
+    };
+    auto commit = [&](auto slot_c, int buf) {
+        constexpr int slot = decltype(slot_c)::value;
+        half8* As = reinterpret_cast<half8*>(smem + buf * STAGE);
+#pragma unroll
+        for (int i = 0; i < A_CH; ++i) As[a_dst[i]] = areg[slot][i];
     };
 
     floatx16 acc[MI][NI];
@@ -203,119 +185,97 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_f16_kernel(GemmArgs p) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    const int nk = kper;
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-        if (s < nk) issue(s, s);
-
-    constexpr int PER_STAGE = A_INSTR + B_INSTR;
-    constexpr int KSTEPS = BK / 16;
-    half8 af[2][MI], bf[2][NI];
-    auto frags = [&](const half8* As, const half8* Bs, int ks, int buf) {
-        const int c = ks * 2 + (lane >> 5);
+    // One k-tile: issue k-tile kt+NS-1 into the register slot consumed one
+    // step ago (past the end, the last k-tile again: in bounds, never used),
+    // multiply from LDS buffer kt%2, write k-tile kt+1 into the other buffer
+    // (last read two steps ago, before the previous barrier), barrier.
+    auto step = [&](int kt, auto slot_c) {
+        constexpr int slot = decltype(slot_c)::value;
+        issue(min(kt + NS - 1, nk - 1), std::integral_constant<int, (slot + NS - 1) % NS>());
+        const half8* As = reinterpret_cast<const half8*>(smem + (kt & 1) * STAGE);
+        half8 af[2][MI];
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
-            const int r = wm * WM + i * 32 + (lane & 31);
-            af[buf][i] = As[r * CHUNKS + (c ^ (r & 7))];
+            const int r = wm * WM + i * 32 + (lane & 31), c = lane >> 5;
+            af[0][i] = As[r * 8 + (c ^ (r & 7))];
         }
 #pragma unroll
-        for (int j = 0; j < NI; ++j) {
-            const int r = wn * WN + j * 32 + (lane & 31);
-            bf[buf][j] = Bs[r * CHUNKS + (c ^ (r & 7))];
-        }
-    };
-    for (int kt = 0; kt < nk; ++kt) {
-        // stage kt has landed once at most (stages issued after it) loads are pending
-        const int after = min(NS - 2, nk - 1 - kt);
-        if (after >= 2) wait_vmcnt<2 * PER_STAGE>();
-        else if (after == 1) wait_vmcnt<PER_STAGE>();
-        else wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();   // every wave's part of stage kt is in LDS, and
-                                        // every wave is done reading stage kt-1
-        asm volatile("" ::: "memory");
-        if (kt + NS - 1 < nk) issue(kt + NS - 1, (kt + NS - 1) % NS);
-
-        const half8* As = reinterpret_cast<const half8*>(smem + (kt % NS) * STAGE_BYTES);
-        const half8* Bs = As + BM * (ROW_BYTES / 16);
-        frags(As, Bs, 0, 0);
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            if (ks + 1 < BK / 16) {
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            if (ks + 1 < KSTEPS) frags(As, Bs, ks + 1, (ks + 1) & 1);   // next k-step's reads in flight
+                for (int i = 0; i < MI; ++i) {
+                    const int r = wm * WM + i * 32 + (lane & 31), c = (ks + 1) * 2 + (lane >> 5);
+                    af[(ks + 1) & 1][i] = As[r * 8 + (c ^ (r & 7))];
+                }
+            }
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < NI; ++j)
-                    acc[i][j] = mfma32x32x16(af[ks & 1][i], bf[ks & 1][j], acc[i][j]);
+                    acc[i][j] = mfma32x32x16(af[ks & 1][i], breg[slot][j][ks], acc[i][j]);
+        }
+        commit(std::integral_constant<int, (slot + 1) % NS>(), (kt + 1) & 1);
+        lds_barrier();
+    };
+
+    issue(0, std::integral_constant<int, 0>());
+    if constexpr (NS > 2) issue(min(1, nk - 1), std::integral_constant<int, 1>());
+    if constexpr (NS > 3) issue(min(2, nk - 1), std::integral_constant<int, 2>());
+    commit(std::integral_constant<int, 0>(), 0);
+    lds_barrier();
+    if constexpr (NK > 0) {
+        static_for<NK>([&](auto kc) {
+            constexpr int kt = decltype(kc)::value;
+            step(kt, std::integral_constant<int, kt % NS>());
+        });
+    } else {
+        for (int kt = 0; kt < nk; kt += NS) {
+            step(kt, std::integral_constant<int, 0>());
+            if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1 % NS>());
+            if constexpr (NS > 2) if (kt + 2 < nk) step(kt + 2, std::integral_constant<int, 2 % NS>());
+            if constexpr (NS > 3) if (kt + 3 < nk) step(kt + 3, std::integral_constant<int, 3 % NS>());
         }
     }
-
-    epilogue<BM, WM, WN, MI, NI, EPI>(p, acc, m0, n0, wm, wn, lane, split);
+    epilogue<MI, NI, EPI>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, m0 + BM <= p.M);
 }
 
-
-template <int BM, int BN, int BK, int WGM, int WGN, int NS, int EPI>
-hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
-    constexpr int lds = NS * (BM + BN) * BK * 2;
-    static bool configured = false;
-    if (!configured) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&gemm_f16_kernel<BM, BN, BK, WGM, WGN, NS, EPI>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e) return e;
-        configured = true;
-    }
-    if (a.splits < 1 || (a.K / BK) % a.splits || a.K % BK || a.N % BN) return hipErrorInvalidValue;
-    if (EPI == EPI_SWIGLU && a.splits != 1) return hipErrorInvalidValue;
-    const int mt = (a.M + BM - 1) / BM, nt = a.N / BN;
-    hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, BK, WGM, WGN, NS, EPI>), dim3(mt * nt * a.splits),
-                       dim3(WGM * WGN * 64), lds, s, a);
+template <int BM, int WN, int WGM, int WGN, int NS, int EPI, int NK>
+hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
+    const int mt = (a.M + BM - 1) / BM, nt = a.N / (WN * WGN);
+    hipLaunchKernelGGL((gemm_kernel<BM, WN, WGM, WGN, NS, EPI, NK>), dim3(mt * nt),
+                       dim3(WGM * WGN * 64), 0, s, a);
     return hipGetLastError();
+}
+
+// The k-tile counts of the hot shapes get the straight-line loop.
+template <int BM, int WN, int WGM, int WGN, int NS, int EPI>
+hipError_t launch_nk(const GemmArgs& a, hipStream_t s) {
+    switch (a.K / BK) {
+        case 48: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 48>(a, s);
+        case 64: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 64>(a, s);
+        case 128: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 128>(a, s);
+        default: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 0>(a, s);
+    }
 }
 
 }  // namespace
 
 bool gemm_shape_ok(int M, int N, int K, int epi) {
     (void)epi;
-    return M > 0 && N > 0 && K > 0 && N % 128 == 0 && K % K_ALIGN == 0;
+    return M > 0 && N > 0 && K > 0 && N % 128 == 0 && K % BK == 0;
 }
 
-// Tile configuration and split-K factor of one projection.  The gate/up
-// projection (N = 2*d_ff) has tiles enough for 256 CUs; the others at
-// prefill batch sizes do not, so their K range is split 2 or 4 ways when
-// that leaves at least 8 (16) k-tiles per split.
-GemmPlan gemm_plan(int M, int N, int K, int epi) {
-    GemmPlan pl{GEMM_CFG_128x128, 1};
-    if (epi == EPI_SWIGLU) {
-        if (M >= 256) pl.cfg = GEMM_CFG_256x128;
-        return pl;
-    }
-    const int tiles = ((M + 127) / 128) * (N / 128);
-    const int nk = K / 64;
-    if (tiles < 256) {
-        if (tiles <= 128 && nk % 4 == 0 && nk / 4 >= 16) pl.splits = 4;
-        else if (nk % 2 == 0 && nk / 2 >= 8) pl.splits = 2;
-    }
-    return pl;
-}
-
+// Tiles (measured on MI355X at the 512-token shapes): the gate/up projection
+// 128 x 128 (four waves of 128 x 32); the stacked q/k/v projection 64 x 256
+// (eight waves of 64 x 32); wo and down 64 x 128 (four waves of 64 x 32).
 hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s) {
     if (!gemm_shape_ok(a.M, a.N, a.K, epi)) return hipErrorInvalidValue;
-    const GemmPlan pl = gemm_plan(a.M, a.N, a.K, epi);
-    GemmArgs g = a;
-    g.splits = pl.splits;
-    if (g.splits > 1 && !g.P) return hipErrorInvalidValue;
-    if (pl.cfg == GEMM_CFG_256x128) {
-        switch (epi) {
-            case EPI_F32: return launch_tile<256, 128, 64, 4, 2, 2, EPI_F32>(g, s);
-            case EPI_RESID: return launch_tile<256, 128, 64, 4, 2, 2, EPI_RESID>(g, s);
-            case EPI_SWIGLU: return launch_tile<256, 128, 64, 4, 2, 2, EPI_SWIGLU>(g, s);
-        }
-    } else {
-        switch (epi) {
-            case EPI_F32: return launch_tile<128, 128, 64, 4, 2, 2, EPI_F32>(g, s);
-            case EPI_RESID: return launch_tile<128, 128, 64, 4, 2, 2, EPI_RESID>(g, s);
-            case EPI_SWIGLU: return launch_tile<128, 128, 64, 4, 2, 2, EPI_SWIGLU>(g, s);
-        }
+    switch (epi) {
+        case EPI_SWIGLU: return launch_nk<128, 32, 1, 4, 4, EPI_SWIGLU>(a, s);
+        case EPI_F32:
+            return a.N % 256 == 0 ? launch_nk<64, 32, 1, 8, 4, EPI_F32>(a, s)
+                                  : launch_nk<64, 32, 1, 4, 4, EPI_F32>(a, s);
+        case EPI_RESID: return launch_nk<64, 32, 1, 4, 4, EPI_RESID>(a, s);
     }
     return hipErrorInvalidValue;
 }

@@ -50,11 +50,16 @@ struct BlobHeader {
 static_assert(sizeof(BlobHeader) == 256, "header is one 256-byte line");
 
 // A packed layer: shapes plus device pointers into the caller's blob.
+// Matrices (logical [rows][cols], y = W x):
 //   wqkv [nqkv][d]   rows: q (hq*hd), k (hkv*hd), v (hkv*hd), gate (hq*hd, gated)
 //   wo   [d][hq*hd]
 //   wgu  [2*f][d]    gate/up interleaved in 16-row blocks: block 2j = gate
 //                    rows 16j..16j+15, block 2j+1 = up rows 16j..16j+15
 //   wd   [d][f]
+// each stored in MFMA-fragment order: the 32 x 16 block (rows 32nb..,
+// cols 16kb..) is 512 consecutive fp16 at ((nb * cols/16) + kb) * 512, and
+// inside it element (32nb + r, 16kb + c) sits at (r + 32*(c/8)) * 8 + c%8 --
+// lane r + 32*(c/8) of a v_mfma_f32_32x32x16_f16 B operand holds it.
 struct ddl_layer {
     int d, hq, hkv, hd, f, nqkv;
     int gated, has_bias, has_qk_norm, rope_on;
@@ -84,25 +89,14 @@ struct GemmArgs {
     float* C; int ldc;          // EPI_F32, EPI_RESID output
     const float* R; int ldr;    // EPI_RESID residual input (may alias C)
     f16* H; int ldh;            // EPI_SWIGLU output [M][N/2]
-    int splits;                 // split-K factor (0 or 1: none); split z > 0 stores
-    float* P;                   // raw partials at P + (z-1)*M*N, [M][N]
 };
-enum { GEMM_CFG_128x128 = 0, GEMM_CFG_256x128 = 1 };
-struct GemmPlan {
-    int cfg;
-    int splits;
-};
-GemmPlan gemm_plan(int M, int N, int K, int epi);
-// Launches with the plan's tile and split-K factor (a.splits is ignored);
-// with splits > 1, a.P must hold (splits-1)*M*N floats.
+// W in MFMA-fragment order (see ddl_layer); N % 128 == 0, K % 64 == 0.
 hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s);
 bool gemm_shape_ok(int M, int N, int K, int epi);
 
-// h = rms_norm(x + P_0 + ... + P_{np-1}) * g as fp16; with np > 0 the completed
-// row is also written to xout (which may alias x).  Partial z is at P + z*rows*d.
-hipError_t launch_rmsnorm_f16(const float* x, const float* P, int np, float* xout, const float* g,
-                              f16* h, int rows, int d, float eps, hipStream_t s);
-hipError_t launch_add_partials(float* x, const float* P, int np, size_t n, hipStream_t s);
+// h = rms_norm(x) * g as fp16, one row of d values per token.
+hipError_t launch_rmsnorm_f16(const float* x, const float* g, f16* h, int rows, int d, float eps,
+                              hipStream_t s);
 
 hipError_t launch_rope_table(float2* tab, int batch, int start_pos, int half, int rot_dim,
                              double theta, hipStream_t s);
@@ -112,8 +106,7 @@ hipError_t launch_rope_table(float2* tab, int batch, int start_pos, int half, in
 //   k16  [hkv][tcap][hd]   key j = cached row j (j < S) or new row j - S
 //   vt16 [hkv][hd][tcap]   the same values transposed
 struct QkvPostArgs {
-    float* qkv; int nqkv;               // [B][nqkv] GEMM output (split 0); gate completed in place
-    const float* P; int np; size_t pstride;   // split-K partials of the GEMM
+    const float* qkv; int nqkv;         // [B][nqkv] GEMM output
     const float* bias;                  // [nqkv] or null
     const float* q_norm; const float* k_norm;   // [hd] or null
     const float2* rope;                 // [B][hd/2] or null
@@ -145,11 +138,18 @@ hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s);
 hipError_t launch_absmax(const void* src, int dtype, size_t n, uint32_t* out_bits,
                          hipStream_t s);
 hipError_t launch_finalize_scales(BlobHeader* hdr, hipStream_t s);
-// Converts a [rows][cols] matrix into fp16 rows of dst (row stride cols):
-// mode 0: dst row = row_offset + r; mode 1/2: gate/up interleave (gate / up).
+// Converts a [rows][cols] matrix into fp16 rows of dst, a matrix of
+// dst_rows x cols stored in MFMA-fragment order: mode 0: dst row =
+// row_offset + r; mode 1/2: gate/up interleave (gate / up).
 hipError_t launch_convert_rows(const void* src, int dtype, int rows, int cols, f16* dst,
                                int row_offset, int mode, const BlobHeader* hdr, int mat,
                                hipStream_t s);
+// Offset (in elements) of element (r, c) of a fragment-ordered matrix with
+// `cols` columns.
+__host__ __device__ inline size_t frag_index(int r, int c, int cols) {
+    return ((size_t)(r >> 5) * (cols >> 4) + (c >> 4)) * 512 + ((r & 31) + 32 * ((c >> 3) & 1)) * 8 +
+           (c & 7);
+}
 
 // decode (one token against the mirror)
 constexpr int DECODE_MAX_SPLITS = 256;
@@ -171,7 +171,7 @@ hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s);
 
 enum { GV_RESID = 0, GV_SWIGLU = 1 };
 struct GemvArgs {
-    const f16* W; int K;         // [rows][K] packed weights (gate/up interleaved for GV_SWIGLU)
+    const f16* W; int K;         // [rows][K] fragment-ordered weights (gate/up interleaved for GV_SWIGLU)
     int N;                       // outputs
     const float* inv_scale;      // device scalar
     const float* x;              // [K]

@@ -13,12 +13,8 @@
 
 namespace {
 
-// One 256-thread block per row; d % 4 == 0.  With np > 0 the row is first
-// completed from split-K partials (x + P_0 + ... + P_{np-1}, in that order)
-// and the completed row is written back to xout.
+// One 256-thread block per row; d % 4 == 0.
 __global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const float* __restrict__ x,
-                                                          const float* __restrict__ P, int np,
-                                                          size_t pstride, float* xout,
                                                           const float* __restrict__ g,
                                                           f16* __restrict__ h, int d, float eps) {
     __shared__ float red[4];
@@ -28,35 +24,16 @@ __global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const float* __restric
     const int n4 = d >> 2;
     float ss = 0.f;
     for (int i = threadIdx.x; i < n4; i += 256) {
-        float4 v = xr[i];
-        for (int z = 0; z < np; ++z) {
-            const float4 q = reinterpret_cast<const float4*>(P + z * pstride + row * d)[i];
-            v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
-        }
-        if (np) reinterpret_cast<float4*>(xout + row * d)[i] = v;
+        const float4 v = xr[i];
         ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
     }
-    ss = block_sum_256(ss, red);   // (its barriers also order the xout writes before the reads)
+    ss = block_sum_256(ss, red);
     const float r = 1.0f / sqrtf(ss / (float)d + eps);
-    const float4* src = np ? reinterpret_cast<const float4*>(xout + row * d) : xr;
     half4* hr = reinterpret_cast<half4*>(h + row * d);
     for (int i = threadIdx.x; i < n4; i += 256) {
-        const float4 v = src[i], w = gr[i];
+        const float4 v = xr[i], w = gr[i];
         hr[i] = half4{(f16)(v.x * r * w.x), (f16)(v.y * r * w.y), (f16)(v.z * r * w.z),
                       (f16)(v.w * r * w.w)};
-    }
-}
-
-// x += P_0 + ... + P_{np-1} (the last layer's split-K partials).
-__global__ __launch_bounds__(256) void add_partials_kernel(float* x, const float* __restrict__ P,
-                                                           int np, size_t n4) {
-    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
-        float4 v = reinterpret_cast<float4*>(x)[i];
-        for (int z = 0; z < np; ++z) {
-            const float4 q = reinterpret_cast<const float4*>(P + z * n4 * 4)[i];
-            v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
-        }
-        reinterpret_cast<float4*>(x)[i] = v;
     }
 }
 
@@ -73,13 +50,13 @@ __global__ void rope_table_kernel(float2* tab, int batch, int start_pos, int hal
 }
 
 // One 256-thread block per (block of 32 tokens, head slot).  Slots: [0, hq)
-// q heads, [hq, hq+hkv) k heads, [hq+hkv, hq+2hkv) v heads, then (gated
-// layers) hq gate heads.  Thread t takes token t/8 and head elements
+// q heads, [hq, hq+hkv) k heads, [hq+hkv, hq+2hkv) v heads (a gated layer's
+// gate columns are read by the attention straight from the projection).  Thread t takes token t/8 and head elements
 // [(t%8)*HD/8, +HD/8); the Neox partner of element e (e < HD/2) lives in
-// thread t^4.  Each value is first completed from the split-K partials.
+// thread t^4.
 // q goes to q16 (fp16), k to the K rows (fp32) and to K16[g][S+b] (fp16),
-// v to the V rows (fp32) and, transposed through LDS, to Vt16[g][e][S+b];
-// the gate is written back in place.  Block index nblk (one past the last
+// v to the V rows (fp32) and, transposed through LDS, to Vt16[g][e][S+b].
+// Block index nblk (one past the last
 // token block) zero-fills K16/Vt16 rows [S+32*nblk, S+32*nblk+32), so every
 // 32-key tile the attention reads is finite.
 template <int HD>
@@ -103,28 +80,15 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs p) {
     const int col0 = slot * HD + e0;     // q, k, v, gate slots are contiguous columns
     if (valid) {
         const float* src = p.qkv + (size_t)b * p.nqkv + col0;
-        const float* psrc = p.P + (size_t)b * p.nqkv + col0;   // partial z at psrc + z*pstride
 #pragma unroll
         for (int i = 0; i < EPT; i += 4) {
-            float4 v = *reinterpret_cast<const float4*>(src + i);
-            for (int z = 0; z < p.np; ++z) {
-                const float4 q = *reinterpret_cast<const float4*>(psrc + z * p.pstride + i);
-                v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
-            }
+            const float4 v = *reinterpret_cast<const float4*>(src + i);
             x[i] = v.x; x[i + 1] = v.y; x[i + 2] = v.z; x[i + 3] = v.w;
         }
-        if (p.bias && slot < p.hq + 2 * p.hkv) {
+        if (p.bias) {
 #pragma unroll
             for (int i = 0; i < EPT; ++i) x[i] += p.bias[col0 + i];
         }
-    }
-    if (slot >= p.hq + 2 * p.hkv) {      // gate: completed value back in place
-        if (valid && p.np) {
-            float* dst = p.qkv + (size_t)b * p.nqkv + col0;
-#pragma unroll
-            for (int i = 0; i < EPT; ++i) dst[i] = x[i];
-        }
-        return;
     }
     if (is_q || is_k) {
         const float* gn = is_q ? p.q_norm : p.k_norm;
@@ -260,7 +224,7 @@ __global__ __launch_bounds__(256) void convert_rows_kernel(const void* src, int 
         const int r = (int)(i / cols), c = (int)(i - (size_t)r * cols);
         int dr = row_offset + r;
         if (mode != 0) dr = (r >> 4) * 32 + (mode - 1) * 16 + (r & 15);
-        dst[(size_t)dr * cols + c] = (f16)ldexpf(load_weight(src, dtype, i), sh);
+        dst[frag_index(dr, c, cols)] = (f16)ldexpf(load_weight(src, dtype, i), sh);
     }
 }
 
@@ -271,16 +235,9 @@ int grid_for(size_t n) {
 
 }  // namespace
 
-hipError_t launch_rmsnorm_f16(const float* x, const float* P, int np, float* xout, const float* g,
-                              f16* h, int rows, int d, float eps, hipStream_t s) {
-    hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3(rows), dim3(256), 0, s, x, P, np,
-                       (size_t)rows * d, xout, g, h, d, eps);
-    return hipGetLastError();
-}
-
-hipError_t launch_add_partials(float* x, const float* P, int np, size_t n, hipStream_t s) {
-    const size_t n4 = n / 4;
-    hipLaunchKernelGGL(add_partials_kernel, dim3(grid_for(n4)), dim3(256), 0, s, x, P, np, n4);
+hipError_t launch_rmsnorm_f16(const float* x, const float* g, f16* h, int rows, int d, float eps,
+                              hipStream_t s) {
+    hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3(rows), dim3(256), 0, s, x, g, h, d, eps);
     return hipGetLastError();
 }
 
@@ -293,7 +250,7 @@ hipError_t launch_rope_table(float2* tab, int batch, int start_pos, int half, in
 }
 
 hipError_t launch_qkv_post(const QkvPostArgs& a, hipStream_t s) {
-    const dim3 grid((a.B + 31) / 32 + 1, (a.gated ? 2 : 1) * a.hq + 2 * a.hkv);
+    const dim3 grid((a.B + 31) / 32 + 1, a.hq + 2 * a.hkv);
     if (a.hd == 128)
         hipLaunchKernelGGL(qkv_post_kernel<128>, grid, dim3(256), 0, s, a);
     else if (a.hd == 64)
