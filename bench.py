@@ -5,14 +5,22 @@ A step is one ddl_prefill_dense_stack call over the whole 28-layer run with
 weights, hidden rows and outputs resident in HBM.  Prints one JSON line:
 tokens/s, the stack's fraction of dense fp16/bf16 MFMA peak, the roofline of
 the dominant kernel (the gate/up projection + SwiGLU GEMM, timed per launch
-with HIP events in a second pass of the same steps) and the CPU oracle timed
-on a bounded sample of the same workload.
+with HIP events in a second pass of the same steps), the single-token decode
+layer at 32768 cached rows (ms per layer, decode attention as a fraction of
+HBM bandwidth) and the CPU oracle timed on a bounded sample of the prefill
+workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+                    [--no-decode] [--copy-calibration]
+
+--copy-calibration adds three plain 1 GiB device-to-device copies at the end,
+the reference a hardware-counter run scales FETCH_SIZE / WRITE_SIZE by.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -39,9 +47,10 @@ def algorithmic_flops(cfg):
     return (gemm + attn) * cfg.n_layers, 2 * cfg.batch * d * 2 * f
 
 
-def cpu_baseline(cfg, n_sample_layers=2):
-    """The oracle (fp64 numpy) on the first layers of the same workload."""
-    import numpy as np
+def cpu_baseline(cfg, budget_s=12.0):
+    """The oracle (fp64 numpy) layer by layer over the same workload until
+    about ``budget_s`` seconds of oracle time (or the whole stack) have run;
+    drawing the inputs is not timed.  Scaled to the whole stack."""
     import oracle
     import synth
     try:
@@ -49,16 +58,100 @@ def cpu_baseline(cfg, n_sample_layers=2):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = os.cpu_count() or 1
-    sub = cfg.replace(n_layers=n_sample_layers)
-    inp = synth.stack_inputs(sub)
-    layers = [{n: synth.values(a) for n, a in w.items()} for w in inp.layers]
-    t0 = time.perf_counter()
-    oracle.prefill_dense_stack(inp.hidden, layers, sub, sub.start_pos, inp.prefix_k, inp.prefix_v)
-    dt = time.perf_counter() - t0
-    per_step = dt * cfg.n_layers / n_sample_layers
-    return {"value": cfg.batch / per_step, "unit": "tok/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n_sample_layers} of {cfg.n_layers} layers at pp{cfg.batch} "
-                      f"(fp64 numpy oracle, {dt:.1f}s), scaled x{cfg.n_layers / n_sample_layers:g}"}
+    x = synth.hidden_rows(cfg)
+    spent, done = 0.0, 0
+    while done < cfg.n_layers and spent < budget_s:
+        w = {n: synth.values(a) for n, a in synth.layer_weights(cfg, done).items()}
+        t0 = time.perf_counter()
+        x, _, _ = oracle.dense_layer(x, w, cfg, cfg.start_pos)
+        spent += time.perf_counter() - t0
+        done += 1
+    per_step = spent * cfg.n_layers / done
+    return {"value": round(cfg.batch / per_step, 2), "unit": "tok/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"first {done} of {cfg.n_layers} layers at pp{cfg.batch} "
+                      f"(fp64 numpy oracle, {spent:.1f}s), scaled x{cfg.n_layers / done:g}"}
+
+
+def gate_up_traffic():
+    """HBM bytes per gate/up launch from the committed hardware-counter
+    summary, or None when the GEMM source has changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "gemm_gate_up_llama3b_pp512_pmc.md")
+    src = os.path.join(ROOT, "dense_decoder_layer_amd", "csrc", "gemm.hip")
+    try:
+        text = open(path).read()
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    want = re.search(r"gemm\.hip sha256: ([0-9a-f]{64})", text)
+    val = re.search(r"traffic bytes per launch: (\d+)", text)
+    if not want or not val or want.group(1) != digest:
+        return None
+    return int(val.group(1))
+
+
+def decode_bench(ddl, ctx, reps=40):
+    """ddl_attn_layer at 32768 cached rows, gated, softcap 50 (one token).
+    Two mirrors alternate so the 268 MB of K/V rows a call reads cannot sit
+    in the 256 MB last-level cache; each call appends its row, as a decode
+    loop does."""
+    import numpy as np
+    import torch
+    import synth
+    from dense_decoder_layer_amd.workloads import desc_for
+    cfg = synth.DECODE_CONFIG
+    inp = synth.decode_inputs(cfg)
+    layer = ddl.pack_layer_from_host(ctx, desc_for(cfg.stack_view()), inp["weights"])
+    cap = ddl.ddl_mirror_plan_capacity(cfg.rows, cfg.rows + reps + 8)
+    mirrors, bufs = [], []
+    k = torch.from_numpy(inp["cache_k"]).cuda()
+    v = torch.from_numpy(inp["cache_v"]).cuda()
+    for _ in range(2):
+        buf = torch.empty(ddl.ddl_mirror_bytes(cfg.n_kv_heads, cfg.head_dim, cap),
+                          dtype=torch.uint8, device="cuda")
+        m = ddl.ddl_mirror_init(buf, cfg.n_kv_heads, cfg.head_dim, cap)
+        assert ddl.ddl_mirror_upload(m, k, v, cfg.rows) == 1
+        mirrors.append(m)
+        bufs.append(buf)
+    del k, v
+    ws = torch.empty(ddl.ddl_attn_workspace_bytes(layer, cap), dtype=torch.uint8, device="cuda")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q, kn, vn, gate, res = (t(inp[n]) for n in ("q", "k", "v", "gate", "residual"))
+    out = torch.empty(cfg.d_model, dtype=torch.float32, device="cuda")
+
+    def call(i):
+        m = mirrors[i % 2]
+        rows = ddl.ddl_mirror_seq_len(m)
+        rc = ddl.ddl_attn_layer(ctx, m, rows, q, kn, vn, gate,
+                                cfg.n_heads, cfg.softcap, layer, res, out, ws)
+        assert rc == 1, ddl.ddl_last_error()
+        return rows + 1                 # rows attended: the cached ones and this token's
+
+    for i in range(4):
+        call(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    start.record(stream)
+    for i in range(reps):
+        call(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    layer_ms = start.elapsed_time(end) / reps
+    ddl.ddl_probe_enable(ctx, ddl.DDL_K_DECODE_ATTN, reps)
+    attended = sum(call(i) for i in range(reps))
+    torch.cuda.synchronize()
+    durs = ddl.ddl_probe_read(ctx, reps)
+    ddl.ddl_probe_enable(ctx, ddl.DDL_K_DECODE_ATTN, 0)
+    attn_ms = sum(durs) / len(durs)
+    attn_bytes = attended * cfg.kv_width * 4 * 2 // reps     # fp32 K and V rows read per call
+    return {"config": f"{cfg.name}: {cfg.rows} cached rows, {cfg.n_heads} q / {cfg.n_kv_heads} "
+                      f"KV heads x {cfg.head_dim}, softcap {cfg.softcap:g}, sigmoid gate, "
+                      f"wo + RMSNorm + SwiGLU {cfg.d_ff} tail, hidden {cfg.d_model}",
+            "ms_per_layer": round(layer_ms, 4), "attn_us": round(attn_ms * 1e3, 2),
+            "attn_bytes": attn_bytes,
+            "attn_hbm_gbs": round(attn_bytes / (attn_ms / 1e3) / 1e9, 1),
+            "attn_hbm_frac": round(attn_bytes / (attn_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
 def main():
@@ -67,6 +160,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the multi-GPU sharding "
@@ -130,8 +225,20 @@ def main():
                      "achieved": round(achieved, 1), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
                      "avg_launch_us": round(gu_ms * 1e3, 2), "launches": len(durs),
-                     "traffic": None},
+                     "traffic": gate_up_traffic()},
     }
+    del stack, bufs
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        log("decode layer at 32768 rows ...")
+        result["decode"] = decode_bench(ddl, ctx)
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample ...")
         result["cpu_baseline"] = cpu_baseline(cfg)

@@ -590,7 +590,7 @@ int ddl_attn_layer(ddl_ctx* ctx, ddl_mirror* m, int host_rows, const float* q, c
     d.part_o = reinterpret_cast<float*>(ws + W.po);
     d.o = o;
     d.R = host_rows; d.hq = L->hq; d.hkv = L->hkv; d.hd = L->hd;
-    decode_split_plan(host_rows + 1, &d.n_splits, &d.rows_per_split);
+    decode_split_plan(L->hq, L->hkv, L->hd, host_rows + 1, &d.n_splits, &d.rows_per_split);
     d.softcap = softcap;
     hipError_t e;
     {

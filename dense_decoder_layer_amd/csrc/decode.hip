@@ -6,20 +6,159 @@
 // The layer tail is x + ffn(rms_norm(x + branch)) with one dense SwiGLU
 // expert ("frink-models 0.49.0 src/fused_layer.rs", module doc).
 //
-// Attention is split over rows: workgroup (split, kv head) walks rows
-// [r0, r1) of the mirror, plus the token's own row (index R, read from the
-// k/v arguments and written into the mirror by the one workgroup whose range
-// holds it), for all query heads of the KV head's group.  Rows are read as
-// fp32 with 16 lanes per row (two 256-byte coalesced segments per row for
-// head_dim 128) and the softmax is online per lane group; the groups and
-// waves are merged in a fixed order and one unnormalised partial (m, l, o)
-// per (query head, split) goes to the workspace.  A second kernel merges
-// the splits in order, normalises and applies the gate.  Everything is
-// fp32 with fp16 weights widened on load.
+// Attention is split over rows.  Main kernel (KV row width hkv*hd of 256,
+// 512 or 1024 floats): one wave reads whole mirror rows -- all KV heads, so
+// each load instruction covers contiguous 128-byte runs of the row -- with
+// hd/DPL lanes per KV head and DPL dims per lane, and keeps an online
+// softmax (running max m, sum l, unnormalised o) for every query head of
+// the lane's KV head.  Split s of n takes rows s, s+n, s+2n, ... (wave w of
+// the split every 8th of them), so at any moment the whole grid streams one
+// contiguous window of the mirror.  The token's own row (index R) comes
+// from the k/v arguments and the wave that takes it also writes it into the
+// mirror.  The eight waves merge through LDS in a fixed tree and one
+// unnormalised partial (m, l, o) per (query head, split) goes to the
+// workspace.  Other row widths use a kernel with one KV head per workgroup
+// (16 lanes per row, contiguous row ranges per split).  A second kernel
+// merges the splits in a fixed order, normalises and applies the gate.
+// Everything is fp32 with fp16 weights widened on load.
 #include "common.h"
 #include "internal.h"
 
 namespace {
+
+constexpr int ROWS_WAVES = 8;      // waves per workgroup of the row-per-wave kernel
+
+template <int HD, int DPL, int G>
+__global__ __launch_bounds__(ROWS_WAVES * 64) void decode_attn_rows_kernel(DecodeAttnArgs p) {
+    constexpr int NW = ROWS_WAVES;
+    constexpr int LPH = HD / DPL;            // lanes per KV head
+    constexpr int HKV = 64 / LPH;            // KV heads of a row
+    constexpr int HQ = HKV * G;
+    constexpr int NC = DPL / 4;              // 16-byte chunks per lane
+    static_assert(LPH * HKV == 64 && DPL % 4 == 0 && G * DPL <= 64, "row covers the wave");
+    __shared__ float so[NW / 2][HQ][HD];
+    __shared__ float sml[NW / 2][HQ][2];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane / LPH, sub = lane % LPH;
+    const int kvw = HKV * HD;
+    const int nrows = p.R + 1;
+    const int split = blockIdx.x, ns = p.n_splits;
+    const float LOG2E = 1.4426950408889634f;
+    // chunk c of the lane: dims c*4*LPH + sub*4 .. +3 of KV head g; q is
+    // pre-scaled by log2(e)/sqrt(hd), so logits come out in the exp2 domain
+    const float qs = LOG2E / sqrtf((float)HD);
+    float q[G][DPL];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const float4 v = *reinterpret_cast<const float4*>(p.q + (size_t)(g * G + h) * HD + c * 4 * LPH + sub * 4);
+            q[h][4 * c] = v.x * qs; q[h][4 * c + 1] = v.y * qs;
+            q[h][4 * c + 2] = v.z * qs; q[h][4 * c + 3] = v.w * qs;
+        }
+    float m[G], l[G], o[G][DPL];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) o[h][i] = 0.f;
+    }
+    const float cap = p.softcap, inv_cap = cap > 0.f ? 1.0f / cap : 0.f;
+    for (int r = split + ns * wave; r < nrows; r += ns * NW) {
+        const float* ks = r < p.R ? p.mk + (size_t)r * kvw : p.knew;
+        const float* vs = r < p.R ? p.mv + (size_t)r * kvw : p.vnew;
+        float kx[DPL], vx[DPL];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const float4 kk = *reinterpret_cast<const float4*>(ks + g * HD + c * 4 * LPH + sub * 4);
+            const float4 vv = *reinterpret_cast<const float4*>(vs + g * HD + c * 4 * LPH + sub * 4);
+            kx[4 * c] = kk.x; kx[4 * c + 1] = kk.y; kx[4 * c + 2] = kk.z; kx[4 * c + 3] = kk.w;
+            vx[4 * c] = vv.x; vx[4 * c + 1] = vv.y; vx[4 * c + 2] = vv.z; vx[4 * c + 3] = vv.w;
+        }
+        if (r == p.R) {   // append this token's row to the mirror
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const size_t at = (size_t)r * kvw + g * HD + c * 4 * LPH + sub * 4;
+                *reinterpret_cast<float4*>(p.mk + at) = make_float4(kx[4 * c], kx[4 * c + 1], kx[4 * c + 2], kx[4 * c + 3]);
+                *reinterpret_cast<float4*>(p.mv + at) = make_float4(vx[4 * c], vx[4 * c + 1], vx[4 * c + 2], vx[4 * c + 3]);
+            }
+        }
+        float sc[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float a = 0.f;
+#pragma unroll
+            for (int i = 0; i < DPL; ++i) a += q[h][i] * kx[i];
+#pragma unroll
+            for (int off = 1; off < LPH; off <<= 1) a += __shfl_xor(a, off, 64);
+            sc[h] = a;
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float v = sc[h];
+            if (cap > 0.f) v = cap * LOG2E * tanhf(v * (inv_cap / LOG2E));
+            const float m_new = fmaxf(m[h], v);
+            const float alpha = exp2f(m[h] - m_new);     // m_new is finite: v is
+            const float pr = exp2f(v - m_new);
+            l[h] = l[h] * alpha + pr;
+            m[h] = m_new;
+#pragma unroll
+            for (int i = 0; i < DPL; ++i) o[h][i] = o[h][i] * alpha + pr * vx[i];
+        }
+    }
+    // waves [half, 2*half) hand their state to waves [0, half) through LDS
+    auto put = [&](int slot) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) so[slot][g * G + h][c * 4 * LPH + sub * 4 + i] = o[h][4 * c + i];
+            if (sub == 0) {
+                sml[slot][g * G + h][0] = m[h];
+                sml[slot][g * G + h][1] = l[h];
+            }
+        }
+    };
+    auto take = [&](int slot) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float mo = sml[slot][g * G + h][0], lo = sml[slot][g * G + h][1];
+            const float mn = fmaxf(m[h], mo);
+            const float mu = mn == -INFINITY ? 0.f : mn;
+            const float a = exp2f(m[h] - mu), b = exp2f(mo - mu);
+            l[h] = l[h] * a + lo * b;
+            m[h] = mn;
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    o[h][4 * c + i] = o[h][4 * c + i] * a + so[slot][g * G + h][c * 4 * LPH + sub * 4 + i] * b;
+        }
+    };
+#pragma unroll
+    for (int half = NW / 2; half >= 1; half >>= 1) {
+        if (wave >= half && wave < 2 * half) put(wave - half);
+        __syncthreads();
+        if (wave < half) take(wave);
+        __syncthreads();
+    }
+    if (wave == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const size_t slot = (size_t)(g * G + h) * ns + split;
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                *reinterpret_cast<float4*>(p.part_o + slot * HD + c * 4 * LPH + sub * 4) =
+                    make_float4(o[h][4 * c], o[h][4 * c + 1], o[h][4 * c + 2], o[h][4 * c + 3]);
+            if (sub == 0) {
+                p.part_m[slot] = m[h];
+                p.part_l[slot] = l[h];
+            }
+        }
+    }
+}
 
 template <int HD, int G>
 __global__ __launch_bounds__(256) void decode_attn_split_kernel(DecodeAttnArgs p) {
@@ -55,61 +194,63 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(DecodeAttnArgs p
         for (int i = 0; i < DPL; ++i) o[h][i] = 0.f;
     }
 
-    for (int base = r0; base < r1; base += 16) {
-        const int r = base + wave * 4 + grp;
-        const bool valid = r < r1;
-        float kx[DPL], vx[DPL];
-        const float* ksrc = nullptr;
-        const float* vsrc = nullptr;
-        if (valid) {
-            if (r < p.R) {
-                ksrc = p.mk + (size_t)r * kvw + g * HD;
-                vsrc = p.mv + (size_t)r * kvw + g * HD;
-            } else {
-                ksrc = p.knew + g * HD;
-                vsrc = p.vnew + g * HD;
-            }
-        }
+    // U groups of 16 rows per pass: every load of the pass is issued before
+    // any of its arithmetic, so each lane keeps 4*U 16-byte loads in flight
+    constexpr int U = 4;
+    for (int base = r0; base < r1; base += 16 * U) {
+        float kx[U][DPL], vx[U][DPL];
+        bool valid[U];
 #pragma unroll
-        for (int j = 0; j < NF4; ++j) {
-            float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
-            if (valid) {
-                kk = *reinterpret_cast<const float4*>(ksrc + j * 64 + sub * 4);
-                vv = *reinterpret_cast<const float4*>(vsrc + j * 64 + sub * 4);
-            }
-            kx[4 * j] = kk.x; kx[4 * j + 1] = kk.y; kx[4 * j + 2] = kk.z; kx[4 * j + 3] = kk.w;
-            vx[4 * j] = vv.x; vx[4 * j + 1] = vv.y; vx[4 * j + 2] = vv.z; vx[4 * j + 3] = vv.w;
-        }
-        if (valid && r == p.R) {   // append this token's row to the mirror
+        for (int u = 0; u < U; ++u) {
+            const int r = base + u * 16 + wave * 4 + grp;
+            valid[u] = r < r1;
+            const float* ksrc = r < p.R ? p.mk + (size_t)r * kvw + g * HD : p.knew + g * HD;
+            const float* vsrc = r < p.R ? p.mv + (size_t)r * kvw + g * HD : p.vnew + g * HD;
 #pragma unroll
             for (int j = 0; j < NF4; ++j) {
-                const size_t at = (size_t)r * kvw + g * HD + j * 64 + sub * 4;
-                *reinterpret_cast<float4*>(p.mk + at) =
-                    make_float4(kx[4 * j], kx[4 * j + 1], kx[4 * j + 2], kx[4 * j + 3]);
-                *reinterpret_cast<float4*>(p.mv + at) =
-                    make_float4(vx[4 * j], vx[4 * j + 1], vx[4 * j + 2], vx[4 * j + 3]);
+                float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
+                if (valid[u]) {
+                    kk = *reinterpret_cast<const float4*>(ksrc + j * 64 + sub * 4);
+                    vv = *reinterpret_cast<const float4*>(vsrc + j * 64 + sub * 4);
+                }
+                kx[u][4 * j] = kk.x; kx[u][4 * j + 1] = kk.y; kx[u][4 * j + 2] = kk.z; kx[u][4 * j + 3] = kk.w;
+                vx[u][4 * j] = vv.x; vx[u][4 * j + 1] = vv.y; vx[u][4 * j + 2] = vv.z; vx[u][4 * j + 3] = vv.w;
             }
         }
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float s = 0.f;
+        for (int u = 0; u < U; ++u) {
+            const int r = base + u * 16 + wave * 4 + grp;
+            if (valid[u] && r == p.R) {   // append this token's row to the mirror
 #pragma unroll
-            for (int i = 0; i < DPL; ++i) s += q[h][i] * kx[i];
-            s += __shfl_xor(s, 1, 64);
-            s += __shfl_xor(s, 2, 64);
-            s += __shfl_xor(s, 4, 64);
-            s += __shfl_xor(s, 8, 64);
-            s *= scale;
-            if (p.softcap > 0.f) s = p.softcap * tanhf(s / p.softcap);
-            s = valid ? s * LOG2E : -INFINITY;
-            const float m_new = fmaxf(m[h], s);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = exp2f(m[h] - m_use);
-            const float pr = exp2f(s - m_use);
-            l[h] = l[h] * alpha + pr;
-            m[h] = m_new;
+                for (int j = 0; j < NF4; ++j) {
+                    const size_t at = (size_t)r * kvw + g * HD + j * 64 + sub * 4;
+                    *reinterpret_cast<float4*>(p.mk + at) =
+                        make_float4(kx[u][4 * j], kx[u][4 * j + 1], kx[u][4 * j + 2], kx[u][4 * j + 3]);
+                    *reinterpret_cast<float4*>(p.mv + at) =
+                        make_float4(vx[u][4 * j], vx[u][4 * j + 1], vx[u][4 * j + 2], vx[u][4 * j + 3]);
+                }
+            }
 #pragma unroll
-            for (int i = 0; i < DPL; ++i) o[h][i] = o[h][i] * alpha + pr * vx[i];
+            for (int h = 0; h < G; ++h) {
+                float sc = 0.f;
+#pragma unroll
+                for (int i = 0; i < DPL; ++i) sc += q[h][i] * kx[u][i];
+                sc += __shfl_xor(sc, 1, 64);
+                sc += __shfl_xor(sc, 2, 64);
+                sc += __shfl_xor(sc, 4, 64);
+                sc += __shfl_xor(sc, 8, 64);
+                sc *= scale;
+                if (p.softcap > 0.f) sc = p.softcap * tanhf(sc / p.softcap);
+                sc = valid[u] ? sc * LOG2E : -INFINITY;
+                const float m_new = fmaxf(m[h], sc);
+                const float m_use = m_new == -INFINITY ? 0.f : m_new;
+                const float alpha = exp2f(m[h] - m_use);
+                const float pr = exp2f(sc - m_use);
+                l[h] = l[h] * alpha + pr;
+                m[h] = m_new;
+#pragma unroll
+                for (int i = 0; i < DPL; ++i) o[h][i] = o[h][i] * alpha + pr * vx[u][i];
+            }
         }
     }
 
@@ -168,23 +309,61 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(DecodeAttnArgs p
     }
 }
 
-// One block per query head, one thread per dim: merge the splits in order,
-// normalise, gate.
+// Merge of the splits: block (query head, 32-dim slice) of 1024 threads =
+// 32 dims x 32 groups of at most 8 splits (n_splits <= 256), so every load
+// of the kernel is issued in one round; each group merges its splits, the
+// groups meet in LDS in a fixed order; normalise, gate.
+constexpr int COMBINE_GROUPS = 32;
+static_assert(COMBINE_GROUPS * 8 >= DECODE_MAX_SPLITS, "eight splits per group at most");
+
 template <int HD>
-__global__ __launch_bounds__(HD) void decode_attn_combine_kernel(DecodeAttnArgs p) {
-    const int h = blockIdx.x, d = threadIdx.x;
-    const size_t base = (size_t)h * p.n_splits;
-    float M = -INFINITY;
-    for (int s = 0; s < p.n_splits; ++s) M = fmaxf(M, p.part_m[base + s]);
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < p.n_splits; ++s) {
-        const float a = exp2f(p.part_m[base + s] - M);
-        L += p.part_l[base + s] * a;
-        O += p.part_o[(base + s) * HD + d] * a;
+__global__ __launch_bounds__(COMBINE_GROUPS * 32) void decode_attn_combine_kernel(DecodeAttnArgs p) {
+    __shared__ float sm_[COMBINE_GROUPS], sl_[COMBINE_GROUPS], so_[COMBINE_GROUPS][33];
+    const int h = blockIdx.x, d0 = blockIdx.y * 32, tid = threadIdx.x;
+    const int d = tid & 31, grp = tid >> 5;
+    const int ns = p.n_splits;
+    const size_t base = (size_t)h * ns;
+    const int per = (ns + COMBINE_GROUPS - 1) / COMBINE_GROUPS;
+    const int s0 = grp * per, s1 = min(ns, s0 + per);
+    float mv[8], lv[8], ov[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const bool ok = s0 + u < s1;
+        mv[u] = ok ? p.part_m[base + s0 + u] : -INFINITY;
+        lv[u] = ok ? p.part_l[base + s0 + u] : 0.f;
+        ov[u] = ok ? p.part_o[(base + s0 + u) * HD + d0 + d] : 0.f;
     }
-    float r = O / L;
-    if (p.gate) r *= 1.0f / (1.0f + expf(-p.gate[(size_t)h * HD + d]));
-    p.o[(size_t)h * HD + d] = r;
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = fmaxf(m, mv[u]);
+    const float mu = m == -INFINITY ? 0.f : m;
+    float l = 0.f, O = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const float w = exp2f(mv[u] - mu);
+        l += lv[u] * w;
+        O += ov[u] * w;
+    }
+    if (d == 0) {
+        sm_[grp] = m;
+        sl_[grp] = l;
+    }
+    so_[grp][d] = O;
+    __syncthreads();
+    if (tid < 32) {
+        float M = -INFINITY;
+        for (int gq = 0; gq < COMBINE_GROUPS; ++gq) M = fmaxf(M, sm_[gq]);
+        const float Mu = M == -INFINITY ? 0.f : M;
+        float L = 0.f, T = 0.f;
+        for (int gq = 0; gq < COMBINE_GROUPS; ++gq) {
+            const float w = exp2f(sm_[gq] - Mu);
+            L += sl_[gq] * w;
+            T += so_[gq][tid] * w;
+        }
+        float r = T / L;
+        if (p.gate) r *= 1.0f / (1.0f + expf(-p.gate[(size_t)h * HD + d0 + tid]));
+        p.o[(size_t)h * HD + d0 + tid] = r;
+    }
 }
 
 // y = W x (fp16 weights times inv_scale, fp32 x) with fused epilogues; W in
@@ -269,10 +448,36 @@ hipError_t launch_split_hd(const DecodeAttnArgs& a, int G, hipStream_t s) {
         case 8: hipLaunchKernelGGL((decode_attn_split_kernel<HD, 8>), grid, dim3(256), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
-    hipError_t e = hipGetLastError();
-    if (e) return e;
-    hipLaunchKernelGGL(decode_attn_combine_kernel<HD>, dim3(a.hq), dim3(HD), 0, s, a);
     return hipGetLastError();
+}
+
+template <int HD, int DPL>
+hipError_t launch_rows_dpl(const DecodeAttnArgs& a, int G, hipStream_t s) {
+    const dim3 grid(a.n_splits), block(ROWS_WAVES * 64);
+    switch (G) {
+        case 1: hipLaunchKernelGGL((decode_attn_rows_kernel<HD, DPL, 1>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((decode_attn_rows_kernel<HD, DPL, 2>), grid, block, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((decode_attn_rows_kernel<HD, DPL, 3>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((decode_attn_rows_kernel<HD, DPL, 4>), grid, block, 0, s, a); break;
+        case 8:
+            if constexpr (8 * DPL <= 64) {
+                hipLaunchKernelGGL((decode_attn_rows_kernel<HD, DPL, 8>), grid, block, 0, s, a);
+                break;
+            }
+            return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int HD>
+hipError_t launch_rows_hd(const DecodeAttnArgs& a, int G, hipStream_t s) {
+    switch (a.hkv * HD) {
+        case 256: return launch_rows_dpl<HD, 4>(a, G, s);
+        case 512: return launch_rows_dpl<HD, 8>(a, G, s);
+        case 1024: return launch_rows_dpl<HD, 16>(a, G, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -283,7 +488,21 @@ bool decode_group_ok(int hq, int hkv, int hd) {
     return (hd == 64 || hd == 128) && (G == 1 || G == 2 || G == 3 || G == 4 || G == 8);
 }
 
-void decode_split_plan(int rows_total, int* n_splits, int* rows_per_split) {
+bool decode_rows_kernel_ok(int hq, int hkv, int hd) {
+    const int w = hkv * hd, G = hq / hkv;
+    return (w == 256 || w == 512 || (w == 1024 && G <= 4));
+}
+
+void decode_split_plan(int hq, int hkv, int hd, int rows_total, int* n_splits, int* rows_per_split) {
+    if (decode_rows_kernel_ok(hq, hkv, hd)) {
+        // interleaved rows: a split is any 1/n of them; 200 workgroups of
+        // eight waves measured best at 32K rows (more run slower)
+        int splits = (rows_total + 63) / 64;
+        splits = splits < 1 ? 1 : (splits > DECODE_ROWS_SPLITS ? DECODE_ROWS_SPLITS : splits);
+        *n_splits = splits;
+        *rows_per_split = (rows_total + splits - 1) / splits;
+        return;
+    }
     int splits = (rows_total + 63) / 64;
     if (splits > DECODE_MAX_SPLITS) splits = DECODE_MAX_SPLITS;
     if (splits < 1) splits = 1;
@@ -295,9 +514,19 @@ void decode_split_plan(int rows_total, int* n_splits, int* rows_per_split) {
 
 hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s) {
     const int G = a.hq / a.hkv;
-    if (a.hd == 128) return launch_split_hd<128>(a, G, s);
-    if (a.hd == 64) return launch_split_hd<64>(a, G, s);
-    return hipErrorInvalidValue;
+    if (a.n_splits < 1 || a.n_splits > DECODE_MAX_SPLITS || a.hd % 32) return hipErrorInvalidValue;
+    const bool rows = decode_rows_kernel_ok(a.hq, a.hkv, a.hd);
+    hipError_t e;
+    if (a.hd == 128) e = rows ? launch_rows_hd<128>(a, G, s) : launch_split_hd<128>(a, G, s);
+    else if (a.hd == 64) e = rows ? launch_rows_hd<64>(a, G, s) : launch_split_hd<64>(a, G, s);
+    else return hipErrorInvalidValue;
+    if (e) return e;
+    const dim3 grid(a.hq, a.hd / 32);
+    if (a.hd == 128)
+        hipLaunchKernelGGL(decode_attn_combine_kernel<128>, grid, dim3(COMBINE_GROUPS * 32), 0, s, a);
+    else
+        hipLaunchKernelGGL(decode_attn_combine_kernel<64>, grid, dim3(COMBINE_GROUPS * 32), 0, s, a);
+    return hipGetLastError();
 }
 
 bool gemv_shape_ok(int K) { return K > 0 && K % 16 == 0 && K <= GV_MAXK; }

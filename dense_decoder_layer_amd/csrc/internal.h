@@ -166,7 +166,9 @@ struct DecodeAttnArgs {
     float softcap;
 };
 bool decode_group_ok(int hq, int hkv, int hd);
-void decode_split_plan(int rows_total, int* n_splits, int* rows_per_split);
+constexpr int DECODE_ROWS_SPLITS = 200;   // split cap of the row-per-wave kernel
+bool decode_rows_kernel_ok(int hq, int hkv, int hd);
+void decode_split_plan(int hq, int hkv, int hd, int rows_total, int* n_splits, int* rows_per_split);
 hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s);
 
 enum { GV_RESID = 0, GV_SWIGLU = 1 };

@@ -108,7 +108,13 @@ def small_cfg(**kw):
 @pytest.mark.parametrize("kw", [dict(), dict(gated=True, softcap=2.0),
                                 dict(n_heads=4, n_kv_heads=4, head_dim=64, rows=0),
                                 dict(n_heads=6, n_kv_heads=2, rows=1000, weight_dtype="fp32"),
-                                dict(n_heads=16, n_kv_heads=2, rows=17)])
+                                dict(n_heads=16, n_kv_heads=2, rows=17),
+                                # KV row widths the row-per-wave kernel does not
+                                # take (128 floats) and the widths it does at
+                                # other group sizes
+                                dict(n_heads=4, n_kv_heads=1, rows=700, softcap=10.0),
+                                dict(n_heads=8, n_kv_heads=8, rows=333, gated=True),
+                                dict(n_heads=16, n_kv_heads=16, head_dim=64, rows=65)])
 def test_decode_shapes(ddl, kw):
     cfg = small_cfg(**kw)
     inp = synth.decode_inputs(cfg)
