@@ -162,6 +162,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--breakdown", action="store_true",
+                    help="also time every prefill kernel class per launch (HIP events)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the multi-GPU sharding "
@@ -207,6 +209,25 @@ def main():
     ddl.ddl_probe_enable(ctx, ddl.DDL_K_GEMM_GATE_UP, 0)
     gu_ms = sum(durs) / len(durs)
 
+    breakdown = None
+    if args.breakdown:
+        kinds = {"rmsnorm": ddl.DDL_K_RMSNORM, "gemm_qkv": ddl.DDL_K_GEMM_QKV,
+                 "qkv_post": ddl.DDL_K_QKV_POST, "attn_prefill": ddl.DDL_K_ATTN_PREFILL,
+                 "gemm_wo": ddl.DDL_K_GEMM_WO, "gemm_gate_up": ddl.DDL_K_GEMM_GATE_UP,
+                 "gemm_down": ddl.DDL_K_GEMM_DOWN}
+        breakdown = {}
+        for name, kind in kinds.items():
+            cap = args.steps * cfg.n_layers * 2
+            ddl.ddl_probe_enable(ctx, kind, cap)
+            for _ in range(args.steps):
+                stack.run(hidden, 0, None, None, bufs)
+            torch.cuda.synchronize()
+            d = ddl.ddl_probe_read(ctx, cap)
+            ddl.ddl_probe_enable(ctx, kind, 0)
+            breakdown[name] = {"avg_us": round(sum(d) / len(d) * 1e3, 2),
+                               "per_step_us": round(sum(d) / args.steps * 1e3, 1)}
+        log("per-kernel: " + json.dumps(breakdown))
+
     flops, gu_flops = algorithmic_flops(cfg)
     tok_s = cfg.batch / (ms / 1e3)
     achieved = gu_flops / (gu_ms / 1e3) / 1e12
@@ -227,6 +248,8 @@ def main():
                      "avg_launch_us": round(gu_ms * 1e3, 2), "launches": len(durs),
                      "traffic": gate_up_traffic()},
     }
+    if breakdown:
+        result["breakdown"] = breakdown
     del stack, bufs
     torch.cuda.empty_cache()
     if not args.no_decode:

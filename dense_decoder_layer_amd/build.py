@@ -18,11 +18,15 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 SOURCES = ["abi.cpp", "gemm.hip", "attn_prefill.hip", "rowops.hip", "decode.hip"]
+# Per-source extras.  The attention kernel's MFMA accumulators are small and
+# rescaled by VALU work every tile: keeping them in arch VGPRs (instead of
+# AGPRs) saves the accvgpr moves.  The GEMMs need the AGPRs for their tiles.
+EXTRA = {"attn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

@@ -5,19 +5,25 @@
 // of "frink-models 0.38.0 src/decoder/device_attention.rs",
 // device_attention_layer).
 //
-// Flash-style, one wave per workgroup: the wave takes 32 queries of one
-// query head and walks the keys of its KV head in tiles of 32 with a running
-// max and sum per query (online softmax, base-2 exponentials).  Keys and
-// values were staged once per layer as fp16: K16 [kv head][key][hd] and
-// Vt16 [kv head][hd][key].  Tiles move global -> LDS by DMA
-// (global_load_lds_dwordx4) through a 3-stage ring, so the next tiles are in
-// flight while one is used; a single wave needs no barriers.  Both products
-// run on v_mfma_f32_32x32x16_f16 in transposed form: S^T = K Q^T gives every
-// lane 16 scores of one query (its partner lane l^32 holds the other 16), and
-// those probabilities are directly the B operand of O^T += V^T P^T; the
-// rescale factor of a query is one scalar per lane.  Tiles wholly above the
-// wave's last query are not visited; masked scores are -inf and contribute
-// exact zeros, so a token's outputs do not depend on later tokens' values.
+// Flash-style: a workgroup takes 32 queries of one query head; its NW waves
+// split the key tiles of the KV head round-robin (wave w takes tiles w,
+// w+NW, ...), each with a running max and sum per query (online softmax,
+// base-2 exponentials), and merge their partial states through LDS in a
+// fixed order at the end.
+//
+// Keys and values were staged once per layer as fp16: K16 [kv head][key][hd]
+// and Vt16 [kv head][hd][key].  Tiles move global -> LDS by DMA
+// (global_load_lds_dwordx4) through a small ring per wave, so the next tile
+// is in flight while one is used; each wave owns its ring, so the loop needs
+// no barriers.  Both products run on v_mfma_f32_32x32x16_f16 in transposed
+// form: S^T = K Q^T gives every lane 16 scores of one query (its partner lane
+// l^32 holds the other 16), and those probabilities are directly the B
+// operand of O^T += V^T P^T; the rescale factor of a query is one scalar per
+// lane.  The running max is raised only when a tile exceeds it by a margin,
+// so rescaling O is rare.  Tiles wholly above the wave's last query are not
+// visited; only tiles on the diagonal or past the last key apply the causal
+// mask, and masked scores are -inf and contribute exact zeros, so a token's
+// outputs do not depend on later tokens' values.
 #include "common.h"
 #include "internal.h"
 
@@ -27,7 +33,26 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int KT = 32;    // keys per tile
-constexpr int NS = 3;     // LDS ring stages
+constexpr int RING = 2;   // LDS ring stages per wave (tiles in flight + 1)
+
+// Waves per workgroup.  Two waves with two-stage rings (64 KB of LDS at
+// head_dim 128) let two workgroups share a CU; measured best against one
+// wave with three stages and three or four waves with two or three stages.
+template <int HD>
+constexpr int attn_waves() { return 2; }
+template <int HD, int NW, int NSTAGE = RING>
+constexpr int attn_lds_bytes() { return NW * NSTAGE * (2 * KT * HD * 2); }
+
+// log2-domain headroom of the running max: it is raised only when a tile's
+// max exceeds it by more than this, so the rescale of O is rare; P stays
+// <= 2^8, exact enough in fp16 (11-bit significand at any magnitude)
+constexpr float MAX_SLACK = 8.0f;
+
+// tanh from one exp2: sign(x) (1 - t) / (1 + t), t = 2^(-2|x| log2 e)
+__device__ __forceinline__ float tanh_exp2(float x) {
+    const float t = __builtin_amdgcn_exp2f(-2.8853900817779268f * fabsf(x));
+    return copysignf((1.0f - t) * __builtin_amdgcn_rcpf(1.0f + t), x);
+}
 
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -41,8 +66,8 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int HD>
-__global__ __launch_bounds__(64) void attn_prefill_kernel(AttnPrefillArgs p) {
+template <int HD, bool CAP, int NW, int NS = RING>
+__global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnPrefillArgs p) {
     constexpr int KCH = HD / 8;                  // 16-byte chunks per K row
     constexpr int K_BYTES = KT * HD * 2;         // K tile [32 keys][HD]
     constexpr int V_BYTES = HD * KT * 2;         // V^T tile [HD][32 keys]
@@ -51,9 +76,12 @@ __global__ __launch_bounds__(64) void attn_prefill_kernel(AttnPrefillArgs p) {
     constexpr int PER = K_INSTR + V_INSTR;       // DMA instructions per tile
     constexpr int KS = HD / 16;                  // k-steps of S^T over the head dim
     constexpr int HB = HD / 32;                  // 32-row blocks of O^T
-    __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
+    extern __shared__ __attribute__((aligned(1024))) char smem_all[];
+    static_assert(NW == 1 || (NW - 1) * (HD * 32 + 64) * 4 <= NW * NS * STAGE, "merge fits the rings");
 
-    const int lane = threadIdx.x, g2 = lane >> 5, ql = lane & 31;
+    const int lane = threadIdx.x & 63, g2 = lane >> 5, ql = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: LDS addresses stay scalar
+    char* smem = smem_all + wave * NS * STAGE;
     const int qt = gridDim.x - 1 - blockIdx.x;     // longest rows first
     const int h = blockIdx.y;
     const int g = h / (p.hq / p.hkv);
@@ -63,8 +91,13 @@ __global__ __launch_bounds__(64) void attn_prefill_kernel(AttnPrefillArgs p) {
     const int nkeys = p.S + p.B;
     const int kv_end = min(p.S + q0 + 32, nkeys);  // keys the wave can see
     const int ntiles = (kv_end + KT - 1) / KT;
+    const int my_n = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;   // this wave's tiles
+    auto tile_of = [&](int i) { return wave + i * NW; };
     const float LOG2E = 1.4426950408889634f;
     const float scale = 1.0f / sqrtf((float)HD);
+    // exp2-domain logit: c * s, or capl * tanh(s * ic) with a softcap
+    const float c = scale * LOG2E;
+    const float capl = p.softcap * LOG2E, ic = CAP ? scale / p.softcap : 0.f;
 
     // Per-lane DMA sources.  K: instruction j covers rows 4j..4j+3 (HD=128)
     // or 8j..8j+7 (HD=64); lane chunk (l % KCH) ^ (row % 8) keeps the K rows
@@ -109,57 +142,77 @@ __global__ __launch_bounds__(64) void attn_prefill_kernel(AttnPrefillArgs p) {
         for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
     float m = -INFINITY, l = 0.f;
 
-    issue(0, 0);
-    issue(min(1, ntiles - 1), 1);
-    for (int t = 0; t < ntiles; ++t) {
-        const int slot = t % NS;
-        // the tile after next goes into the slot used two tiles ago (or the
-        // last tile again, into that already-used slot: same wait count on
+    if (my_n > 0) {
+#pragma unroll
+        for (int j = 0; j < NS - 1; ++j) issue(tile_of(min(j, my_n - 1)), j);
+    }
+    for (int i = 0; i < my_n; ++i) {
+        const int slot = i % NS;
+        // tile i+NS-1 goes into the slot used one tile ago (or the wave's
+        // last tile again, into an already-used slot: the same wait count on
         // every path)
-        issue(min(t + 2, ntiles - 1), (t + 2) % NS);
-        wait_vmcnt<2 * PER>();            // tile t has landed in LDS
+        issue(tile_of(min(i + NS - 1, my_n - 1)), (i + NS - 1) % NS);
+        wait_vmcnt<(NS - 1) * PER>();     // tile i has landed in LDS
         asm volatile("" ::: "memory");
         const half8* Ks = reinterpret_cast<const half8*>(smem + slot * STAGE);
         const f16* Vs = reinterpret_cast<const f16*>(smem + slot * STAGE + K_BYTES);
-        const int k0 = t * KT;
+        const int k0 = tile_of(i) * KT;
 
-        // S^T[key][query]: A = K rows, B = Q^T
-        floatx16 st;
+        // S^T[key][query]: A = K rows, B = Q^T; two independent chains
+        floatx16 st0, st1;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) st[e] = 0.f;
+        for (int e = 0; e < 16; ++e) st0[e] = st1[e] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int c = ks * 2 + g2;
-            st = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ks[ql * KCH + (c ^ (ql & 7))], qf[ks], st,
-                                                        0, 0, 0);
+        for (int ks = 0; ks < KS; ks += 2) {
+            const int c0 = ks * 2 + g2, c1 = c0 + 2;
+            st0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ks[ql * KCH + (c0 ^ (ql & 7))], qf[ks], st0, 0, 0, 0);
+            st1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ks[ql * KCH + (c1 ^ (ql & 7))], qf[ks + 1], st1, 0, 0, 0);
         }
-        // lane holds key k0 + 8*(e/4) + 4*g2 + e%4 of query qrow
-        float tmax = -INFINITY;
+        // lane holds key k0 + 8*(e/4) + 4*g2 + e%4 of query qrow.  Without a
+        // softcap the scores stay raw (the exp2-domain scale c > 0 keeps
+        // their order) and c is folded into the exponent's fma below.
+        float sv[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int kpos = k0 + 8 * (e >> 2) + 4 * g2 + (e & 3);
-            float v = st[e] * scale;
-            if (p.softcap > 0.f) v = p.softcap * tanhf(v / p.softcap);
-            v *= LOG2E;
-            if (kpos > qpos || kpos >= nkeys) v = -INFINITY;
-            st[e] = v;
-            tmax = fmaxf(tmax, v);
+            const float r = st0[e] + st1[e];
+            sv[e] = CAP ? capl * tanh_exp2(r * ic) : r;
         }
+        // only a tile that reaches past the block's first query or past the
+        // last key needs the mask (a wave-uniform test)
+        if (k0 + KT - 1 > p.S + q0 || k0 + KT > nkeys) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int kpos = k0 + 8 * (e >> 2) + 4 * g2 + (e & 3);
+                sv[e] = ((kpos <= qpos) & (kpos < nkeys)) ? sv[e] : -INFINITY;
+            }
+        }
+        float tmax = sv[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, sv[e]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float m_new = fmaxf(m, tmax);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2f(m - m_use);
+        if constexpr (!CAP) tmax *= c;
+        // raise the running max (and rescale l and O) only past the slack;
+        // the branch is uniform over the wave
+        const bool grow = tmax > m + MAX_SLACK;
+        if (__ballot(grow)) {
+            // lanes that keep their max scale by 1; from -inf the factor is 0
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m - tmax) : 1.0f;
+            l *= alpha;
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) o[hb] = o[hb] * alpha;
+            if (grow) m = tmax;
+        }
+        const float m_use = m == -INFINITY ? 0.f : m;                 // every key so far masked
         float psum = 0.f;
         half8 pf[2];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const float pv = exp2f(st[e] - m_use);
+            const float pv = __builtin_amdgcn_exp2f(CAP ? sv[e] - m_use : fmaf(sv[e], c, -m_use));
             psum += pv;
             pf[e >> 3][e & 7] = (f16)pv;
         }
         psum += __shfl_xor(psum, 32, 64);
-        l = l * alpha + psum;
-        m = m_new;
+        l += psum;
         // O^T[hd][query] += V^T P^T.  P^T operand kh: element j of lane group
         // g2 is key kh*16 + (j < 4 ? 4*g2 + j : 8 + 4*g2 + j - 4), which is
         // exactly score e = 8*kh + j above; the V^T operand reads the same keys.
@@ -168,7 +221,6 @@ __global__ __launch_bounds__(64) void attn_prefill_kernel(AttnPrefillArgs p) {
             const int r = hb * 32 + ql;
             const f16* vrow = Vs + r * KT;
             const int sw = (r >> 1) & 3;
-            o[hb] = o[hb] * alpha;
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
                 const half4 lo = *reinterpret_cast<const half4*>(vrow + (((2 * kh) ^ sw) * 8) + 4 * g2);
@@ -179,6 +231,42 @@ __global__ __launch_bounds__(64) void attn_prefill_kernel(AttnPrefillArgs p) {
         }
     }
     wait_vmcnt<0>();
+
+    // merge: waves 1..NW-1 leave (m, l, O^T) in LDS, wave 0 folds them in
+    // order.  Every wave's DMA has landed, so the rings can be reused.
+    __syncthreads();
+    float* mbuf = reinterpret_cast<float*>(smem_all);                 // [NW-1][32]
+    float* lbuf = mbuf + (NW - 1) * 32;                               // [NW-1][32]
+    float* obuf = lbuf + (NW - 1) * 32;                               // [NW-1][HD][32]
+    if (wave > 0) {
+        if (g2 == 0) {
+            mbuf[(wave - 1) * 32 + ql] = m;
+            lbuf[(wave - 1) * 32 + ql] = l;
+        }
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = hb * 32 + 8 * (e >> 2) + 4 * g2 + (e & 3);
+                obuf[((size_t)(wave - 1) * HD + r) * 32 + ql] = o[hb][e];
+            }
+    }
+    __syncthreads();
+    if (wave > 0) return;
+    for (int w = 1; w < NW; ++w) {
+        const float mo = mbuf[(w - 1) * 32 + ql], lo = lbuf[(w - 1) * 32 + ql];
+        const float mn = fmaxf(m, mo);              // finite: tile 0 holds key 0
+        const float a = __builtin_amdgcn_exp2f(m - mn), b = __builtin_amdgcn_exp2f(mo - mn);
+        l = l * a + lo * b;
+        m = mn;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = hb * 32 + 8 * (e >> 2) + 4 * g2 + (e & 3);
+                o[hb][e] = o[hb][e] * a + obuf[((size_t)(w - 1) * HD + r) * 32 + ql] * b;
+            }
+    }
 
     if (qrow >= p.B) return;
     const float inv_l = 1.0f / l;
@@ -201,14 +289,26 @@ __global__ __launch_bounds__(64) void attn_prefill_kernel(AttnPrefillArgs p) {
 
 }  // namespace
 
+namespace {
+template <int HD, bool CAP>
+hipError_t launch_hd(const AttnPrefillArgs& a, hipStream_t s) {
+    constexpr int NW = attn_waves<HD>();
+    constexpr int lds = attn_lds_bytes<HD, NW, RING>();
+    // the rings take more than the default 64 KB of dynamic LDS
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&attn_prefill_kernel<HD, CAP, NW>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (attr != hipSuccess) return attr;
+    const dim3 grid((a.B + 31) / 32, a.hq);
+    hipLaunchKernelGGL((attn_prefill_kernel<HD, CAP, NW>), grid, dim3(NW * 64), lds, s, a);
+    return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s) {
     if (a.tcap % 32 || a.tcap < a.S + a.B) return hipErrorInvalidValue;
-    const dim3 grid((a.B + 31) / 32, a.hq);
-    if (a.hd == 128)
-        hipLaunchKernelGGL(attn_prefill_kernel<128>, grid, dim3(64), 0, s, a);
-    else if (a.hd == 64)
-        hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, dim3(64), 0, s, a);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
+    const bool cap = a.softcap > 0.f;
+    if (a.hd == 128) return cap ? launch_hd<128, true>(a, s) : launch_hd<128, false>(a, s);
+    if (a.hd == 64) return cap ? launch_hd<64, true>(a, s) : launch_hd<64, false>(a, s);
+    return hipErrorInvalidValue;
 }
