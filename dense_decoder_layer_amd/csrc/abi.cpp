@@ -49,6 +49,7 @@ const char* why_unsupported(const ddl_layer_desc* d) {
     if (d->head_dim != 64 && d->head_dim != 128) return "head_dim other than 64 or 128";
     if (d->n_heads % d->n_kv_heads != 0) return "n_heads not a multiple of n_kv_heads";
     if (d->d_model % 128 != 0) return "d_model not a multiple of 128";
+    if (d->d_model > 4096) return "d_model above 4096 (the row norm holds a row in registers)";
     if (d->d_ff % 64 != 0) return "d_ff not a multiple of 64";
     if (!(d->attn_softcap >= 0.0f)) return "negative softcap";
     const int nqkv = (d->gated ? 2 : 1) * d->n_heads * d->head_dim + 2 * d->n_kv_heads * d->head_dim;

@@ -13,7 +13,11 @@
 
 namespace {
 
-// One 256-thread block per row; d % 4 == 0.
+// One 256-thread block per row; d % 4 == 0, d <= 4096.  The row and the
+// gains are loaded once into registers (one memory round trip), reduced,
+// normalised and stored as fp16.
+constexpr int RMS_V4 = 4;   // float4s per thread: 256 * 4 * 4 = 4096 columns
+
 __global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const float* __restrict__ x,
                                                           const float* __restrict__ g,
                                                           f16* __restrict__ h, int d, float eps) {
@@ -22,18 +26,25 @@ __global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const float* __restric
     const float4* xr = reinterpret_cast<const float4*>(x + row * d);
     const float4* gr = reinterpret_cast<const float4*>(g);
     const int n4 = d >> 2;
-    float ss = 0.f;
-    for (int i = threadIdx.x; i < n4; i += 256) {
-        const float4 v = xr[i];
-        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    float4 v[RMS_V4], w[RMS_V4];
+#pragma unroll
+    for (int k = 0; k < RMS_V4; ++k) {
+        const int i = threadIdx.x + k * 256;
+        v[k] = i < n4 ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        w[k] = i < n4 ? gr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < RMS_V4; ++k) ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
     ss = block_sum_256(ss, red);
     const float r = 1.0f / sqrtf(ss / (float)d + eps);
     half4* hr = reinterpret_cast<half4*>(h + row * d);
-    for (int i = threadIdx.x; i < n4; i += 256) {
-        const float4 v = xr[i], w = gr[i];
-        hr[i] = half4{(f16)(v.x * r * w.x), (f16)(v.y * r * w.y), (f16)(v.z * r * w.z),
-                      (f16)(v.w * r * w.w)};
+#pragma unroll
+    for (int k = 0; k < RMS_V4; ++k) {
+        const int i = threadIdx.x + k * 256;
+        if (i < n4)
+            hr[i] = half4{(f16)(v[k].x * r * w[k].x), (f16)(v[k].y * r * w[k].y),
+                          (f16)(v[k].z * r * w[k].z), (f16)(v[k].w * r * w[k].w)};
     }
 }
 
@@ -117,9 +128,11 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs p) {
     }
     if (is_q) {
         if (valid) {
-            f16* dst = p.q16 + (size_t)b * p.hq * HD + slot * HD + e0;
+            half8* dst = reinterpret_cast<half8*>(p.q16 + (size_t)b * p.hq * HD + slot * HD + e0);
 #pragma unroll
-            for (int i = 0; i < EPT; ++i) dst[i] = (f16)x[i];
+            for (int i = 0; i < EPT; i += 8)
+                dst[i / 8] = half8{(f16)x[i], (f16)x[i + 1], (f16)x[i + 2], (f16)x[i + 3],
+                                   (f16)x[i + 4], (f16)x[i + 5], (f16)x[i + 6], (f16)x[i + 7]};
         }
         return;
     }
@@ -131,9 +144,11 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs p) {
             for (int i = 0; i < EPT; i += 4)
                 *reinterpret_cast<float4*>(dst + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
         }
-        f16* kd = p.k16 + ((size_t)g * p.tcap + key) * HD + e0;
+        half8* kd = reinterpret_cast<half8*>(p.k16 + ((size_t)g * p.tcap + key) * HD + e0);
 #pragma unroll
-        for (int i = 0; i < EPT; ++i) kd[i] = (f16)x[i];     // zeros past B
+        for (int i = 0; i < EPT; i += 8)                      // zeros past B
+            kd[i / 8] = half8{(f16)x[i], (f16)x[i + 1], (f16)x[i + 2], (f16)x[i + 3],
+                              (f16)x[i + 4], (f16)x[i + 5], (f16)x[i + 6], (f16)x[i + 7]};
         return;
     }
     // v
@@ -237,6 +252,7 @@ int grid_for(size_t n) {
 
 hipError_t launch_rmsnorm_f16(const float* x, const float* g, f16* h, int rows, int d, float eps,
                               hipStream_t s) {
+    if (d % 4 || d > 256 * 4 * RMS_V4) return hipErrorInvalidValue;
     hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3(rows), dim3(256), 0, s, x, g, h, d, eps);
     return hipGetLastError();
 }
