@@ -102,7 +102,7 @@ def decode_bench(ddl, ctx, reps=40):
     cfg = synth.DECODE_CONFIG
     inp = synth.decode_inputs(cfg)
     layer = ddl.pack_layer_from_host(ctx, desc_for(cfg.stack_view()), inp["weights"])
-    cap = ddl.ddl_mirror_plan_capacity(cfg.rows, cfg.rows + reps + 8)
+    cap = ddl.ddl_mirror_plan_capacity(cfg.rows, cfg.rows + 6 * reps + 16)   # every call appends a row
     mirrors, bufs = [], []
     k = torch.from_numpy(inp["cache_k"]).cuda()
     v = torch.from_numpy(inp["cache_v"]).cuda()
@@ -144,6 +144,16 @@ def decode_bench(ddl, ctx, reps=40):
     durs = ddl.ddl_probe_read(ctx, reps)
     ddl.ddl_probe_enable(ctx, ddl.DDL_K_DECODE_ATTN, 0)
     attn_ms = sum(durs) / len(durs)
+    tail = {}
+    for name, kind in (("gemv_wo", ddl.DDL_K_GEMV_WO), ("gemv_gate_up", ddl.DDL_K_GEMV_GATE_UP),
+                       ("gemv_down", ddl.DDL_K_GEMV_DOWN)):
+        ddl.ddl_probe_enable(ctx, kind, reps)
+        for i in range(reps):
+            call(i)
+        torch.cuda.synchronize()
+        d = ddl.ddl_probe_read(ctx, reps)
+        ddl.ddl_probe_enable(ctx, kind, 0)
+        tail[name + "_us"] = round(sum(d) / len(d) * 1e3, 2)
     attn_bytes = attended * cfg.kv_width * 4 * 2 // reps     # fp32 K and V rows read per call
     return {"config": f"{cfg.name}: {cfg.rows} cached rows, {cfg.n_heads} q / {cfg.n_kv_heads} "
                       f"KV heads x {cfg.head_dim}, softcap {cfg.softcap:g}, sigmoid gate, "
@@ -151,7 +161,8 @@ def decode_bench(ddl, ctx, reps=40):
             "ms_per_layer": round(layer_ms, 4), "attn_us": round(attn_ms * 1e3, 2),
             "attn_bytes": attn_bytes,
             "attn_hbm_gbs": round(attn_bytes / (attn_ms / 1e3) / 1e9, 1),
-            "attn_hbm_frac": round(attn_bytes / (attn_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+            "attn_hbm_frac": round(attn_bytes / (attn_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+            "tail": tail}
 
 
 def main():
