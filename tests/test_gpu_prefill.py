@@ -97,6 +97,18 @@ SMALL_CASES = {
                           start_pos=200, d_ff=2816),
     "group3-fp32": small("group3-fp32", n_heads=6, n_kv_heads=2, d_model=768, batch=96,
                          weight_dtype="fp32", softcap=5.0),
+    # eight query heads per KV head, softcap, a ragged batch over a prefix
+    "group8-softcap-b333-prefix64": small("group8-softcap-b333-prefix64", n_heads=16,
+                                          n_kv_heads=2, d_model=1024, batch=333, start_pos=64,
+                                          softcap=50.0, d_ff=1536),
+    # head_dim 64 with a prefix and the output gate
+    "hd64-gated-prefix40": small("hd64-gated-prefix40", n_heads=8, n_kv_heads=4, head_dim=64,
+                                 batch=45, start_pos=40, gated=True),
+    # fewer new tokens than one 32-key tile, over a prefix that is not tile-aligned
+    "b5-prefix70": small("b5-prefix70", batch=5, start_pos=70),
+    # the 3B layer width and heads, a ragged batch over a ragged prefix
+    "llama3b-2layers-b300-prefix777": synth.STACK_CONFIGS["llama3b_pp512"].replace(
+        n_layers=2, batch=300, start_pos=777),
 }
 
 
