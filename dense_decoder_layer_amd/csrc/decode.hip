@@ -495,8 +495,9 @@ bool decode_rows_kernel_ok(int hq, int hkv, int hd) {
 
 void decode_split_plan(int hq, int hkv, int hd, int rows_total, int* n_splits, int* rows_per_split) {
     if (decode_rows_kernel_ok(hq, hkv, hd)) {
-        // interleaved rows: a split is any 1/n of them; 200 workgroups of
-        // eight waves measured best at 32K rows (more run slower)
+        // interleaved rows: a split is any 1/n of them.  At 32K rows,
+        // 176..200 workgroups of eight waves measured best; from about 208
+        // the time rises by a tenth
         int splits = (rows_total + 63) / 64;
         splits = splits < 1 ? 1 : (splits > DECODE_ROWS_SPLITS ? DECODE_ROWS_SPLITS : splits);
         *n_splits = splits;

@@ -166,7 +166,7 @@ struct DecodeAttnArgs {
     float softcap;
 };
 bool decode_group_ok(int hq, int hkv, int hd);
-constexpr int DECODE_ROWS_SPLITS = 200;   // split cap of the row-per-wave kernel
+constexpr int DECODE_ROWS_SPLITS = 184;   // split cap of the row-per-wave kernel
 bool decode_rows_kernel_ok(int hq, int hkv, int hd);
 void decode_split_plan(int hq, int hkv, int hd, int rows_total, int* n_splits, int* rows_per_split);
 hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s);
