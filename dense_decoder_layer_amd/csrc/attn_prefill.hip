@@ -27,6 +27,8 @@
 #include "common.h"
 #include "internal.h"
 
+#include <atomic>
+
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -294,11 +296,18 @@ template <int HD, bool CAP>
 hipError_t launch_hd(const AttnPrefillArgs& a, hipStream_t s) {
     constexpr int NW = attn_waves<HD>();
     constexpr int lds = attn_lds_bytes<HD, NW, RING>();
-    // the rings take more than the default 64 KB of dynamic LDS
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&attn_prefill_kernel<HD, CAP, NW>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (attr != hipSuccess) return attr;
+    // the rings may take more than the default 64 KB of dynamic LDS; the
+    // attribute is set once per device (idempotent if two threads race)
+    static std::atomic<bool> set_on[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64 || !set_on[dev].load(std::memory_order_acquire)) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_prefill_kernel<HD, CAP, NW>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        if (dev >= 0 && dev < 64) set_on[dev].store(true, std::memory_order_release);
+    }
     const dim3 grid((a.B + 31) / 32, a.hq);
     hipLaunchKernelGGL((attn_prefill_kernel<HD, CAP, NW>), grid, dim3(NW * 64), lds, s, a);
     return hipGetLastError();

@@ -86,7 +86,10 @@ void ddl_ctx_destroy(ddl_ctx* ctx);
  *   head_dim; window == 0; no post-attention/post-FFN norm, sinks, ALiBi or
  *   LoRA; rope either disabled or Neox with rot_dim == head_dim, mscale == 1
  *   and no frequency factors; head_dim in {64, 128}; n_heads a multiple of
- *   n_kv_heads; d_model and d_ff multiples of 64. */
+ *   n_kv_heads; d_model a multiple of 128 and at most 4096; d_ff a multiple
+ *   of 64; the stacked q/k/v(/gate) width a multiple of 128; softcap >= 0.
+ *   ddl_attn_layer further needs n_heads / n_kv_heads in {1, 2, 3, 4, 8}
+ *   and d_model, d_ff, n_heads*head_dim at most 15872 (declined otherwise). */
 typedef struct {
     int d_model, n_heads, n_kv_heads, head_dim, v_head_dim, d_ff;
     float rms_eps, post_norm_eps;
@@ -142,9 +145,9 @@ void ddl_layer_destroy(ddl_layer* layer);
 
 /* Workspace bytes a prefill of up to max_batch tokens at a start position of
  * up to max_start_pos needs over `n` layers (0 on bad arguments).  The
- * workspace holds the per-layer intermediates, the layer's keys and values
- * staged as fp16, and split-K partial sums; its contents do not outlive a
- * call. */
+ * workspace holds the per-layer intermediates (normed rows, q/k/v, attention
+ * output, SwiGLU activations) and the layer's keys and values staged as
+ * fp16; its contents do not outlive a call. */
 size_t ddl_workspace_bytes(const ddl_layer* const* layers, int n, int max_batch,
                            int max_start_pos);
 
@@ -165,7 +168,8 @@ size_t ddl_workspace_bytes(const ddl_layer* const* layers, int n, int max_batch,
  *               [batch][n_kv_heads*head_dim] fp32 out: the rows the caller
  *               pushes into its cache, row b for token b (post bias, QK-norm
  *               and RoPE for K)
- *   workspace   >= ddl_workspace_bytes(layers, run, batch) bytes, device
+ *   workspace   device, workspace_bytes >= ddl_workspace_bytes(layers,
+ *               n_layers, batch, start_pos) (else DDL_ERR_WORKSPACE)
  * Returns run_len > 0 (layers 0..run_len-1 ran; hidden_out is the output
  * of layer run_len-1 and k_rows/v_rows[0..run_len-1] are written), 0 when
  * declined (batch < min_batch, layer 0 not servable or its prefix count
