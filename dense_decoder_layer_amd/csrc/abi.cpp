@@ -10,6 +10,8 @@
 
 #include "internal.h"
 
+#include <algorithm>
+
 namespace {
 
 thread_local std::string g_err;
@@ -87,7 +89,7 @@ void blob_layout(const ddl_layer_desc* d, BlobLayout* L) {
 
 // Per-call scratch in the caller's workspace.
 struct WsLayout {
-    size_t rope, h, qkv, q16, o16, x1, a16, k16, vt16, total;
+    size_t rope, h, qkv, q16, o16, x1, a16, k16, vt16, part, total;
     int tcap;
 };
 
@@ -114,6 +116,18 @@ WsLayout ws_layout(const ddl_layer* L, int B, int S) {
     w.a16 = take((size_t)B * L->f * 2);
     w.k16 = take((size_t)L->hkv * w.tcap * L->hd * 2);
     w.vt16 = take((size_t)L->hkv * w.tcap * L->hd * 2);
+    // split-K partials, reused by the QKV, wo and down projections in turn.
+    // A smaller batch may split more ways, so the region covers every batch
+    // up to B (the split only changes at multiples of the 64-row tile).
+    size_t part = 0;
+    for (int b = 64; b < B + 64; b += 64) {
+        const int bb = std::min(b, B);
+        const size_t pq = (size_t)(gemm_splits(bb, L->nqkv, L->d, EPI_F32) - 1) * bb * L->nqkv;
+        const size_t po = (size_t)(gemm_splits(bb, L->d, L->hq * L->hd, EPI_RESID) - 1) * bb * L->d;
+        const size_t pd = (size_t)(gemm_splits(bb, L->d, L->f, EPI_RESID) - 1) * bb * L->d;
+        part = std::max(part, std::max(pq, std::max(po, pd)));
+    }
+    w.part = take(part * 4);
     w.total = o;
     return w;
 }
@@ -365,17 +379,27 @@ int ddl_prefill_dense_stack(ddl_ctx* ctx, const float* hidden, const ddl_layer* 
     f16* a16 = reinterpret_cast<f16*>(ws + W.a16);
     f16* k16 = reinterpret_cast<f16*>(ws + W.k16);
     f16* vt16 = reinterpret_cast<f16*>(ws + W.vt16);
+    float* part = reinterpret_cast<float*>(ws + W.part);
     const int d = L0->d, hq = L0->hq, hkv = L0->hkv, hd = L0->hd, f = L0->f, nqkv = L0->nqkv;
+    // K splits of the projections (gate/up never splits); a split GEMM's
+    // partial sums are added by the kernel that consumes its output: the QKV
+    // post-step, the FFN norm, the next layer's attention norm.  The run's
+    // last down projection does not split, so hidden_out is complete.
+    const int sp_qkv = gemm_splits(batch, nqkv, d, EPI_F32);
+    const int sp_wo = gemm_splits(batch, d, hq * hd, EPI_RESID);
+    const int sp_down = gemm_splits(batch, d, f, EPI_RESID);
+    int pending = 0;                  // partials of the last down projection
 
     hipError_t e = hipSuccess;
     if (L0->rope_on) e = launch_rope_table(rope, batch, start_pos, hd / 2, hd, L0->theta, s);
     for (int l = 0; l < run && !e; ++l) {
         const ddl_layer* L = layers[l];
-        const float* x = l == 0 ? hidden : hidden_out;
+        // the first layer reads the caller's hidden (no partials: never written)
+        float* x = l == 0 ? const_cast<float*>(hidden) : hidden_out;
         // attention branch: x1 = x + wo . attn(rope(qkv(rms_norm(x))))
         {
             ProbeScope p(ctx, DDL_K_RMSNORM, s);
-            e = launch_rmsnorm_f16(x, L->g_attn, h, batch, d, L->eps, s);
+            e = launch_rmsnorm_f16(x, L->g_attn, h, batch, d, L->eps, part, pending, s);
         }
         if (!e && start_pos > 0) {
             StagePrefixArgs sp{};
@@ -389,13 +413,13 @@ int ddl_prefill_dense_stack(ddl_ctx* ctx, const float* hidden, const ddl_layer* 
             g.A = h; g.lda = d; g.W = L->wqkv; g.ldw = d;
             g.M = batch; g.N = nqkv; g.K = d;
             g.inv_scale = &L->hdr->inv_scale[MAT_QKV];
-            g.C = qkv; g.ldc = nqkv;
+            g.C = qkv; g.ldc = nqkv; g.P = part;
             ProbeScope p(ctx, DDL_K_GEMM_QKV, s);
-            e = launch_gemm(g, EPI_F32, s);
+            e = launch_gemm(g, EPI_F32, sp_qkv, s);
         }
         if (!e) {
             QkvPostArgs q{};
-            q.qkv = qkv; q.nqkv = nqkv;
+            q.qkv = qkv; q.nqkv = nqkv; q.part = part; q.nparts = sp_qkv - 1;
             q.bias = L->bqkv; q.q_norm = L->q_norm; q.k_norm = L->k_norm;
             q.rope = L->rope_on ? rope : nullptr;
             q.B = batch; q.S = start_pos; q.hq = hq; q.hkv = hkv; q.hd = hd; q.gated = L->gated;
@@ -421,14 +445,14 @@ int ddl_prefill_dense_stack(ddl_ctx* ctx, const float* hidden, const ddl_layer* 
             g.A = o16; g.lda = hq * hd; g.W = L->wo; g.ldw = hq * hd;
             g.M = batch; g.N = d; g.K = hq * hd;
             g.inv_scale = &L->hdr->inv_scale[MAT_O];
-            g.C = x1; g.ldc = d; g.R = x; g.ldr = d;
+            g.C = x1; g.ldc = d; g.R = x; g.ldr = d; g.P = part;
             ProbeScope p(ctx, DDL_K_GEMM_WO, s);
-            e = launch_gemm(g, EPI_RESID, s);
+            e = launch_gemm(g, EPI_RESID, sp_wo, s);
         }
         // FFN branch: out = x1 + down(silu(gate(h2)) * up(h2)), h2 = rms_norm(x1)
         if (!e) {
             ProbeScope p(ctx, DDL_K_RMSNORM, s);
-            e = launch_rmsnorm_f16(x1, L->g_ffn, h, batch, d, L->eps, s);
+            e = launch_rmsnorm_f16(x1, L->g_ffn, h, batch, d, L->eps, part, sp_wo - 1, s);
         }
         if (!e) {
             GemmArgs g{};
@@ -437,16 +461,18 @@ int ddl_prefill_dense_stack(ddl_ctx* ctx, const float* hidden, const ddl_layer* 
             g.inv_scale = &L->hdr->inv_scale[MAT_GU];
             g.H = a16; g.ldh = f;
             ProbeScope p(ctx, DDL_K_GEMM_GATE_UP, s);
-            e = launch_gemm(g, EPI_SWIGLU, s);
+            e = launch_gemm(g, EPI_SWIGLU, 1, s);
         }
         if (!e) {
             GemmArgs g{};
             g.A = a16; g.lda = f; g.W = L->wd; g.ldw = f;
             g.M = batch; g.N = d; g.K = f;
             g.inv_scale = &L->hdr->inv_scale[MAT_D];
-            g.C = hidden_out; g.ldc = d; g.R = x1; g.ldr = d;
+            g.C = hidden_out; g.ldc = d; g.R = x1; g.ldr = d; g.P = part;
+            const int sp = l + 1 < run ? sp_down : 1;
             ProbeScope p(ctx, DDL_K_GEMM_DOWN, s);
-            e = launch_gemm(g, EPI_RESID, s);
+            e = launch_gemm(g, EPI_RESID, sp, s);
+            pending = sp - 1;
         }
     }
     if (e) return fail(DDL_ERR_DEVICE, std::string("prefill launch: ") + hipGetErrorString(e));

@@ -70,7 +70,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // rows 8*(e/4) + 4*(l/32) + e%4 for e = 0..15.
 template <int MI, int NI, int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, floatx16 (&acc)[MI][NI], int row0,
-                                         int col0, int lane, bool full) {
+                                         int col0, int lane, bool full, int split) {
     const float sc = *p.inv_scale;
     const int rbase = row0 + 4 * (lane >> 5);
     const int cl = lane & 31;
@@ -107,6 +107,15 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, floatx16 (&acc)[MI][
                 float v[16];
 #pragma unroll
                 for (int e = 0; e < 16; ++e) v[e] = acc[i][j][e] * sc;
+                if (split > 0) {         // a later K slice: raw partial for the consumer
+                    float* P = p.P + (size_t)(split - 1) * p.M * p.ldc;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
+                        if (full || row < p.M) P[(size_t)row * p.ldc + col] = v[e];
+                    }
+                    continue;
+                }
                 if constexpr (EPI == EPI_RESID) {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
@@ -124,9 +133,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, floatx16 (&acc)[MI][
 }
 
 // Workgroup of WGM x WGN waves, tile BM x (WN*WGN); wave tile (BM/WGM) x WN.
-// NK > 0: K/64 == NK, straight-line k-loop; NK == 0: generic loop.
+// The grid is tiles x splits; slice z takes k-tiles [z*nk, (z+1)*nk).
+// NK > 0: nk == NK, straight-line k-loop; NK == 0: generic loop.
 template <int BM, int WN, int WGM, int WGN, int NS, int EPI, int NK>
-__global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p, int splits) {
     constexpr int NT = WGM * WGN * 64, BN = WN * WGN, WM = BM / WGM;
     constexpr int MI = WM / 32, NI = WN / 32;
     constexpr int A_CH = BM * 8 / NT;               // 16-byte activation chunks per thread per k-tile
@@ -138,24 +148,26 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
-    const int mt = (p.M + BM - 1) / BM, nt = p.N / BN, total = mt * nt;
+    const int mt = (p.M + BM - 1) / BM, nt = p.N / BN, total = mt * nt * splits;
     int bid = blockIdx.x;
     if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
-    const int m0 = (bid % mt) * BM, n0 = (bid / mt) * BN;
-    const int nk = NK > 0 ? NK : p.K / BK;
+    const int tile = bid % (mt * nt), split = bid / (mt * nt);
+    const int m0 = (tile % mt) * BM, n0 = (tile / mt) * BN;
+    const int nk = NK > 0 ? NK : p.K / BK / splits;
+    const int kt0 = split * nk;                    // this slice's first k-tile
 
     const f16* a_src[A_CH];
     int a_dst[A_CH];                                // half8 index in an LDS slot
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
         const int idx = i * NT + tid, r = idx >> 3, c = idx & 7;
-        a_src[i] = p.A + (size_t)min(m0 + r, p.M - 1) * p.lda + c * 8;   // rows past M: discarded outputs
+        a_src[i] = p.A + (size_t)min(m0 + r, p.M - 1) * p.lda + (size_t)kt0 * BK + c * 8;   // rows past M: discarded outputs
         a_dst[i] = r * 8 + (c ^ (r & 7));
     }
     const f16* wfrag[NI];
 #pragma unroll
     for (int j = 0; j < NI; ++j)
-        wfrag[j] = p.W + (size_t)((n0 + wn * WN) / 32 + j) * (p.K / 16) * 512 + lane * 8;
+        wfrag[j] = p.W + ((size_t)((n0 + wn * WN) / 32 + j) * (p.K / 16) + (size_t)kt0 * 4) * 512 + lane * 8;
 
     half8 areg[NS][A_CH];
     half8 breg[NS][NI][BK / 16];
@@ -236,25 +248,27 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p) {
             if constexpr (NS > 3) if (kt + 3 < nk) step(kt + 3, std::integral_constant<int, 3 % NS>());
         }
     }
-    epilogue<MI, NI, EPI>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, m0 + BM <= p.M);
+    epilogue<MI, NI, EPI>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, m0 + BM <= p.M, split);
 }
 
 template <int BM, int WN, int WGM, int WGN, int NS, int EPI, int NK>
-hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_cfg(const GemmArgs& a, int splits, hipStream_t s) {
     const int mt = (a.M + BM - 1) / BM, nt = a.N / (WN * WGN);
-    hipLaunchKernelGGL((gemm_kernel<BM, WN, WGM, WGN, NS, EPI, NK>), dim3(mt * nt),
-                       dim3(WGM * WGN * 64), 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<BM, WN, WGM, WGN, NS, EPI, NK>), dim3(mt * nt * splits),
+                       dim3(WGM * WGN * 64), 0, s, a, splits);
     return hipGetLastError();
 }
 
-// The k-tile counts of the hot shapes get the straight-line loop.
+// The k-tile counts per slice of the hot shapes get the straight-line loop.
 template <int BM, int WN, int WGM, int WGN, int NS, int EPI>
-hipError_t launch_nk(const GemmArgs& a, hipStream_t s) {
-    switch (a.K / BK) {
-        case 48: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 48>(a, s);
-        case 64: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 64>(a, s);
-        case 128: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 128>(a, s);
-        default: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 0>(a, s);
+hipError_t launch_nk(const GemmArgs& a, int splits, hipStream_t s) {
+    switch (a.K / BK / splits) {
+        case 24: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 24>(a, splits, s);
+        case 32: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 32>(a, splits, s);
+        case 48: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 48>(a, splits, s);
+        case 64: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 64>(a, splits, s);
+        case 128: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 128>(a, splits, s);
+        default: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 0>(a, splits, s);
     }
 }
 
@@ -265,17 +279,32 @@ bool gemm_shape_ok(int M, int N, int K, int epi) {
     return M > 0 && N > 0 && K > 0 && N % 128 == 0 && K % BK == 0;
 }
 
-// Tiles (measured on MI355X at the 512-token shapes): the gate/up projection
-// 128 x 128 (four waves of 128 x 32); the stacked q/k/v projection 64 x 256
-// (eight waves of 64 x 32); wo and down 64 x 128 (four waves of 64 x 32).
-hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s) {
+// Tiles and K splits (measured on MI355X at the 512-token shapes).  The
+// gate/up projection: 128 x 128 tiles (four waves of 128 x 32), 512
+// workgroups, no split (SwiGLU needs the whole sum).  The other projections
+// have too few output tiles to fill 256 CUs; they take 64 x 128 tiles (four
+// waves of 64 x 32, three workgroups fit a CU) and their K range is split
+// until the grid fills the 768 workgroup slots, each slice keeping at least
+// 24 k-tiles (wo split four ways was no faster once its norm adds three
+// partials instead of one).
+int gemm_splits(int M, int N, int K, int epi) {
+    if (epi == EPI_SWIGLU || N % 128) return 1;
+    const int tiles = ((M + 63) / 64) * (N / 128), nk = K / BK;
+    int splits = 1;
+    while (splits < 4 && tiles * splits * 2 <= 768 && nk % (splits * 2) == 0 &&
+           nk / (splits * 2) >= 24)
+        splits *= 2;
+    return splits;
+}
+
+hipError_t launch_gemm(const GemmArgs& a, int epi, int splits, hipStream_t s) {
     if (!gemm_shape_ok(a.M, a.N, a.K, epi)) return hipErrorInvalidValue;
+    if (splits < 1 || (a.K / BK) % splits || (splits > 1 && (!a.P || epi == EPI_SWIGLU)))
+        return hipErrorInvalidValue;
     switch (epi) {
-        case EPI_SWIGLU: return launch_nk<128, 32, 1, 4, 4, EPI_SWIGLU>(a, s);
-        case EPI_F32:
-            return a.N % 256 == 0 ? launch_nk<64, 32, 1, 8, 4, EPI_F32>(a, s)
-                                  : launch_nk<64, 32, 1, 4, 4, EPI_F32>(a, s);
-        case EPI_RESID: return launch_nk<64, 32, 1, 4, 4, EPI_RESID>(a, s);
+        case EPI_SWIGLU: return launch_nk<128, 32, 1, 4, 4, EPI_SWIGLU>(a, 1, s);
+        case EPI_F32: return launch_nk<64, 32, 1, 4, 4, EPI_F32>(a, splits, s);
+        case EPI_RESID: return launch_nk<64, 32, 1, 4, 4, EPI_RESID>(a, splits, s);
     }
     return hipErrorInvalidValue;
 }

@@ -89,14 +89,24 @@ struct GemmArgs {
     float* C; int ldc;          // EPI_F32, EPI_RESID output
     const float* R; int ldr;    // EPI_RESID residual input (may alias C)
     f16* H; int ldh;            // EPI_SWIGLU output [M][N/2]
+    // Split-K (EPI_F32, EPI_RESID): slice 0 of the K range applies the
+    // epilogue to C; slice z > 0 stores its raw scaled sum to
+    // P + (z - 1) * M * ldc, [M][ldc], which the consumer adds in.
+    float* P;
 };
 // W in MFMA-fragment order (see ddl_layer); N % 128 == 0, K % 64 == 0.
-hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s);
+// splits: gemm_splits(...) slices; P must hold (splits - 1) * M * ldc floats.
+hipError_t launch_gemm(const GemmArgs& a, int epi, int splits, hipStream_t s);
 bool gemm_shape_ok(int M, int N, int K, int epi);
+// The K split launch_gemm is to be called with for this shape (1 = none).
+int gemm_splits(int M, int N, int K, int epi);
 
 // h = rms_norm(x) * g as fp16, one row of d values per token.
-hipError_t launch_rmsnorm_f16(const float* x, const float* g, f16* h, int rows, int d, float eps,
-                              hipStream_t s);
+// h = fp16(rms_norm(x) * g).  With nparts > 0, x first gets the split-K
+// partials part[z * rows * d + row * d + col] (z < nparts) added and the sum
+// is written back to x.
+hipError_t launch_rmsnorm_f16(float* x, const float* g, f16* h, int rows, int d, float eps,
+                              const float* part, int nparts, hipStream_t s);
 
 hipError_t launch_rope_table(float2* tab, int batch, int start_pos, int half, int rot_dim,
                              double theta, hipStream_t s);
@@ -106,7 +116,9 @@ hipError_t launch_rope_table(float2* tab, int batch, int start_pos, int half, in
 //   k16  [hkv][tcap][hd]   key j = cached row j (j < S) or new row j - S
 //   vt16 [hkv][hd][tcap]   the same values transposed
 struct QkvPostArgs {
-    const float* qkv; int nqkv;         // [B][nqkv] GEMM output
+    const float* part; int nparts;       // split-K partials of qkv, [nparts][B][nqkv]
+    float* qkv; int nqkv;               // [B][nqkv] GEMM output (a gated layer's
+                                        // gate columns get the partials added in place)
     const float* bias;                  // [nqkv] or null
     const float* q_norm; const float* k_norm;   // [hd] or null
     const float2* rope;                 // [B][hd/2] or null

@@ -18,12 +18,16 @@ namespace {
 // normalised and stored as fp16.
 constexpr int RMS_V4 = 4;   // float4s per thread: 256 * 4 * 4 = 4096 columns
 
-__global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const float* __restrict__ x,
+// With nparts > 0 the split-K partials of the GEMM that produced x are
+// added first (in slice order) and the sum is written back to x.
+__global__ __launch_bounds__(256) void rmsnorm_f16_kernel(float* __restrict__ x,
                                                           const float* __restrict__ g,
-                                                          f16* __restrict__ h, int d, float eps) {
+                                                          f16* __restrict__ h, int d, float eps,
+                                                          const float* __restrict__ part,
+                                                          int nparts, size_t pstride) {
     __shared__ float red[4];
     const size_t row = blockIdx.x;
-    const float4* xr = reinterpret_cast<const float4*>(x + row * d);
+    float4* xr = reinterpret_cast<float4*>(x + row * d);
     const float4* gr = reinterpret_cast<const float4*>(g);
     const int n4 = d >> 2;
     float4 v[RMS_V4], w[RMS_V4];
@@ -32,6 +36,24 @@ __global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const float* __restric
         const int i = threadIdx.x + k * 256;
         v[k] = i < n4 ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
         w[k] = i < n4 ? gr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (nparts > 0) {
+        for (int z = 0; z < nparts; ++z) {
+            const float4* pr = reinterpret_cast<const float4*>(part + z * pstride + row * d);
+#pragma unroll
+            for (int k = 0; k < RMS_V4; ++k) {
+                const int i = threadIdx.x + k * 256;
+                if (i < n4) {
+                    const float4 q = pr[i];
+                    v[k].x += q.x; v[k].y += q.y; v[k].z += q.z; v[k].w += q.w;
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < RMS_V4; ++k) {
+            const int i = threadIdx.x + k * 256;
+            if (i < n4) xr[i] = v[k];
+        }
     }
     float ss = 0.f;
 #pragma unroll
@@ -80,10 +102,12 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs p) {
     const int b = blk * 32 + tl;
     const bool is_q = slot < p.hq, is_k = !is_q && slot < p.hq + p.hkv;
     const bool is_v = !is_q && !is_k && slot < p.hq + 2 * p.hkv;
+    const bool is_gate = !is_q && !is_k && !is_v;     // launched only with partials to add
     const int g = is_k ? slot - p.hq : (is_v ? slot - p.hq - p.hkv : 0);
     const int e0 = part * EPT;
     const bool valid = blk < nblk && b < p.B;
     if (blk == nblk && !is_k && !is_v) return;
+    if (is_gate && !valid) return;
 
     float x[EPT];
 #pragma unroll
@@ -95,6 +119,21 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs p) {
         for (int i = 0; i < EPT; i += 4) {
             const float4 v = *reinterpret_cast<const float4*>(src + i);
             x[i] = v.x; x[i + 1] = v.y; x[i + 2] = v.z; x[i + 3] = v.w;
+        }
+        for (int z = 0; z < p.nparts; ++z) {
+            const float* ps = p.part + ((size_t)z * p.B + b) * p.nqkv + col0;
+#pragma unroll
+            for (int i = 0; i < EPT; i += 4) {
+                const float4 v = *reinterpret_cast<const float4*>(ps + i);
+                x[i] += v.x; x[i + 1] += v.y; x[i + 2] += v.z; x[i + 3] += v.w;
+            }
+        }
+        if (is_gate) {          // the attention reads the gate from the projection
+            float* dst = p.qkv + (size_t)b * p.nqkv + col0;
+#pragma unroll
+            for (int i = 0; i < EPT; i += 4)
+                *reinterpret_cast<float4*>(dst + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
+            return;
         }
         if (p.bias) {
 #pragma unroll
@@ -250,10 +289,11 @@ int grid_for(size_t n) {
 
 }  // namespace
 
-hipError_t launch_rmsnorm_f16(const float* x, const float* g, f16* h, int rows, int d, float eps,
-                              hipStream_t s) {
-    if (d % 4 || d > 256 * 4 * RMS_V4) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3(rows), dim3(256), 0, s, x, g, h, d, eps);
+hipError_t launch_rmsnorm_f16(float* x, const float* g, f16* h, int rows, int d, float eps,
+                              const float* part, int nparts, hipStream_t s) {
+    if (d % 4 || d > 256 * 4 * RMS_V4 || (nparts > 0 && !part)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3(rows), dim3(256), 0, s, x, g, h, d, eps, part,
+                       nparts, (size_t)rows * d);
     return hipGetLastError();
 }
 
@@ -266,7 +306,11 @@ hipError_t launch_rope_table(float2* tab, int batch, int start_pos, int half, in
 }
 
 hipError_t launch_qkv_post(const QkvPostArgs& a, hipStream_t s) {
-    const dim3 grid((a.B + 31) / 32 + 1, a.hq + 2 * a.hkv);
+    if (a.nparts > 0 && !a.part) return hipErrorInvalidValue;
+    // the gate heads (a gated layer's second q half) take part only to get
+    // their split-K partials added
+    const int slots = a.hq + 2 * a.hkv + (a.gated && a.nparts > 0 ? a.hq : 0);
+    const dim3 grid((a.B + 31) / 32 + 1, slots);
     if (a.hd == 128)
         hipLaunchKernelGGL(qkv_post_kernel<128>, grid, dim3(256), 0, s, a);
     else if (a.hd == 64)
