@@ -109,6 +109,10 @@ SMALL_CASES = {
     # the 3B layer width and heads, a ragged batch over a ragged prefix
     "llama3b-2layers-b300-prefix777": synth.STACK_CONFIGS["llama3b_pp512"].replace(
         n_layers=2, batch=300, start_pos=777),
+    # gated and soft-capped at the 3B width: the stacked q/k/v/gate projection
+    # is split over K, so the gate columns get their partial sums added
+    "llama3b-gated-softcap-2layers-b256": synth.STACK_CONFIGS["llama3b_pp512"].replace(
+        n_layers=2, batch=256, gated=True, softcap=30.0),
 }
 
 
