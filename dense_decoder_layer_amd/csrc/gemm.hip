@@ -279,19 +279,32 @@ bool gemm_shape_ok(int M, int N, int K, int epi) {
     return M > 0 && N > 0 && K > 0 && N % 128 == 0 && K % BK == 0;
 }
 
-// Tiles and K splits (measured on MI355X at the 512-token shapes).  The
-// gate/up projection: 128 x 128 tiles (four waves of 128 x 32), 512
-// workgroups, no split (SwiGLU needs the whole sum).  The other projections
-// have too few output tiles to fill 256 CUs; they take 64 x 128 tiles (four
-// waves of 64 x 32, three workgroups fit a CU) and their K range is split
-// until the grid fills the 768 workgroup slots, each slice keeping at least
-// 24 k-tiles (wo split four ways was no faster once its norm adds three
-// partials instead of one).
+// Tiles and K splits (measured on MI355X at the 512-token shapes).
+//  * gate/up and the stacked QKV projection, N a multiple of 256 and more
+//    than 64 rows: 128 x 256 tiles, eight waves of 128 x 32 sharing one
+//    activation tile (a third fewer bytes per flop than two 128 x 128
+//    workgroups on a CU), 3-deep register prefetch; one workgroup per CU.
+//    gate/up is not split (SwiGLU needs the whole sum); QKV has 80 such
+//    tiles and splits K in two (160 workgroups beat 640 smaller ones).
+//  * Otherwise 64 x 128 tiles (four waves of 64 x 32, three workgroups fit
+//    a CU), gate/up 128 x 128.
+//  Splits double while the grid stays within the workgroup slots (768 for
+//  the small tile, 256 for the wide one) and each slice keeps at least 24
+//  k-tiles (wo split four ways was no faster once its norm adds three
+//  partials instead of one).
+namespace {
+bool wide_tile(int M, int N, int epi) {
+    return (epi == EPI_SWIGLU || epi == EPI_F32) && M > 64 && N % 256 == 0;
+}
+}  // namespace
+
 int gemm_splits(int M, int N, int K, int epi) {
     if (epi == EPI_SWIGLU || N % 128) return 1;
-    const int tiles = ((M + 63) / 64) * (N / 128), nk = K / BK;
+    const bool wide = wide_tile(M, N, epi);
+    const int tiles = wide ? ((M + 127) / 128) * (N / 256) : ((M + 63) / 64) * (N / 128);
+    const int slots = wide ? 256 : 768, nk = K / BK;
     int splits = 1;
-    while (splits < 4 && tiles * splits * 2 <= 768 && nk % (splits * 2) == 0 &&
+    while (splits < 4 && tiles * splits * 2 <= slots && nk % (splits * 2) == 0 &&
            nk / (splits * 2) >= 24)
         splits *= 2;
     return splits;
@@ -301,9 +314,14 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, int splits, hipStream_t s) {
     if (!gemm_shape_ok(a.M, a.N, a.K, epi)) return hipErrorInvalidValue;
     if (splits < 1 || (a.K / BK) % splits || (splits > 1 && (!a.P || epi == EPI_SWIGLU)))
         return hipErrorInvalidValue;
+    const bool wide = wide_tile(a.M, a.N, epi);
     switch (epi) {
-        case EPI_SWIGLU: return launch_nk<128, 32, 1, 4, 4, EPI_SWIGLU>(a, 1, s);
-        case EPI_F32: return launch_nk<64, 32, 1, 4, 4, EPI_F32>(a, splits, s);
+        case EPI_SWIGLU:
+            if (wide) return launch_nk<128, 32, 1, 8, 3, EPI_SWIGLU>(a, 1, s);
+            return launch_nk<128, 32, 1, 4, 4, EPI_SWIGLU>(a, 1, s);
+        case EPI_F32:
+            if (wide) return launch_nk<128, 32, 1, 8, 3, EPI_F32>(a, splits, s);
+            return launch_nk<64, 32, 1, 4, 4, EPI_F32>(a, splits, s);
         case EPI_RESID: return launch_nk<64, 32, 1, 4, 4, EPI_RESID>(a, splits, s);
     }
     return hipErrorInvalidValue;
