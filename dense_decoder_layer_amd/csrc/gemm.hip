@@ -286,23 +286,20 @@ bool gemm_shape_ok(int M, int N, int K, int epi) {
 //    workgroups on a CU), 3-deep register prefetch; one workgroup per CU.
 //    gate/up is not split (SwiGLU needs the whole sum); QKV has 80 such
 //    tiles and splits K in two (160 workgroups beat 640 smaller ones).
-//  * Otherwise 64 x 128 tiles (four waves of 64 x 32, three workgroups fit
-//    a CU), gate/up 128 x 128.
-//  Splits double while the grid stays within the workgroup slots (768 for
-//  the small tile, 256 for the wide one) and each slice keeps at least 24
-//  k-tiles (wo split four ways was no faster once its norm adds three
-//  partials instead of one).
+//  * The residual projections take 64 x 128 tiles (four waves of 64 x 32,
+//    three workgroups fit a CU) and split K until the grid fills the 768
+//    workgroup slots, each slice keeping at least 24 k-tiles.  Where K is
+//    too short for a four-way split (wo), 64 x 256 tiles of eight waves
+//    with a two-way split are faster than more, smaller workgroups.
+//  * Anything else: 64 x 128 tiles, gate/up 128 x 128.
 namespace {
-bool wide_tile(int M, int N, int epi) {
-    return (epi == EPI_SWIGLU || epi == EPI_F32) && M > 64 && N % 256 == 0;
-}
-}  // namespace
+enum Tile { T64x128, T128x128, T128x256, T64x256 };
+struct Plan {
+    Tile tile;
+    int splits;
+};
 
-int gemm_splits(int M, int N, int K, int epi) {
-    if (epi == EPI_SWIGLU || N % 128) return 1;
-    const bool wide = wide_tile(M, N, epi);
-    const int tiles = wide ? ((M + 127) / 128) * (N / 256) : ((M + 63) / 64) * (N / 128);
-    const int slots = wide ? 256 : 768, nk = K / BK;
+int split_count(int tiles, int slots, int nk) {
     int splits = 1;
     while (splits < 4 && tiles * splits * 2 <= slots && nk % (splits * 2) == 0 &&
            nk / (splits * 2) >= 24)
@@ -310,19 +307,38 @@ int gemm_splits(int M, int N, int K, int epi) {
     return splits;
 }
 
+Plan gemm_plan(int M, int N, int K, int epi) {
+    const int nk = K / BK;
+    if (epi == EPI_SWIGLU) return {N % 256 == 0 && M > 64 ? T128x256 : T128x128, 1};
+    if (epi == EPI_F32 && N % 256 == 0 && M > 64)
+        return {T128x256, split_count(((M + 127) / 128) * (N / 256), 256, nk)};
+    const int splits = split_count(((M + 63) / 64) * (N / 128), 768, nk);
+    if (epi == EPI_RESID && splits < 4 && N % 256 == 0)
+        return {T64x256, split_count(((M + 63) / 64) * (N / 256), 256, nk)};
+    return {T64x128, splits};
+}
+}  // namespace
+
+int gemm_splits(int M, int N, int K, int epi) {
+    if (!gemm_shape_ok(M, N, K, epi)) return 1;
+    return gemm_plan(M, N, K, epi).splits;
+}
+
 hipError_t launch_gemm(const GemmArgs& a, int epi, int splits, hipStream_t s) {
     if (!gemm_shape_ok(a.M, a.N, a.K, epi)) return hipErrorInvalidValue;
     if (splits < 1 || (a.K / BK) % splits || (splits > 1 && (!a.P || epi == EPI_SWIGLU)))
         return hipErrorInvalidValue;
-    const bool wide = wide_tile(a.M, a.N, epi);
+    const Tile t = gemm_plan(a.M, a.N, a.K, epi).tile;
     switch (epi) {
         case EPI_SWIGLU:
-            if (wide) return launch_nk<128, 32, 1, 8, 3, EPI_SWIGLU>(a, 1, s);
+            if (t == T128x256) return launch_nk<128, 32, 1, 8, 3, EPI_SWIGLU>(a, 1, s);
             return launch_nk<128, 32, 1, 4, 4, EPI_SWIGLU>(a, 1, s);
         case EPI_F32:
-            if (wide) return launch_nk<128, 32, 1, 8, 3, EPI_F32>(a, splits, s);
+            if (t == T128x256) return launch_nk<128, 32, 1, 8, 3, EPI_F32>(a, splits, s);
             return launch_nk<64, 32, 1, 4, 4, EPI_F32>(a, splits, s);
-        case EPI_RESID: return launch_nk<64, 32, 1, 4, 4, EPI_RESID>(a, splits, s);
+        case EPI_RESID:
+            if (t == T64x256) return launch_nk<64, 32, 1, 8, 3, EPI_RESID>(a, splits, s);
+            return launch_nk<64, 32, 1, 4, 4, EPI_RESID>(a, splits, s);
     }
     return hipErrorInvalidValue;
 }
