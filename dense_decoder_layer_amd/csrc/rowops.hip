@@ -83,18 +83,21 @@ __global__ void rope_table_kernel(float2* tab, int batch, int start_pos, int hal
 }
 
 // One 256-thread block per (block of 32 tokens, head slot).  Slots: [0, hq)
-// q heads, [hq, hq+hkv) k heads, [hq+hkv, hq+2hkv) v heads (a gated layer's
-// gate columns are read by the attention straight from the projection).  Thread t takes token t/8 and head elements
-// [(t%8)*HD/8, +HD/8); the Neox partner of element e (e < HD/2) lives in
-// thread t^4.
+// q heads, [hq, hq+hkv) k heads, [hq+hkv, hq+2hkv) v heads, then (a gated
+// layer with split-K partials only) the gate heads, whose summed columns are
+// written back into the projection for the attention to read.  Thread t
+// takes token t/8 and, for i = 0 .. HD/32-1, the four head elements
+// 32i + 4(t%8) .. +3: the eight threads of a token read its 128-byte runs
+// together, and the Neox partner of element e (e < HD/2) is element
+// e + HD/2 of the same thread.
 // q goes to q16 (fp16), k to the K rows (fp32) and to K16[g][S+b] (fp16),
 // v to the V rows (fp32) and, transposed through LDS, to Vt16[g][e][S+b].
-// Block index nblk (one past the last
-// token block) zero-fills K16/Vt16 rows [S+32*nblk, S+32*nblk+32), so every
-// 32-key tile the attention reads is finite.
-template <int HD>
+// Block index nblk (one past the last token block) zero-fills K16/Vt16 rows
+// [S+32*nblk, S+32*nblk+32), so every 32-key tile the attention reads is
+// finite.  NP: split-K partial slices added (in slice order).
+template <int HD, int NP>
 __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs p) {
-    constexpr int EPT = HD / 8;          // elements per thread
+    constexpr int NG = HD / 32;          // float4 groups per thread
     __shared__ f16 vt[HD][33];
     const int tid = threadIdx.x, tl = tid >> 3, part = tid & 7;
     const int blk = blockIdx.x, slot = blockIdx.y;
@@ -102,42 +105,46 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs p) {
     const int b = blk * 32 + tl;
     const bool is_q = slot < p.hq, is_k = !is_q && slot < p.hq + p.hkv;
     const bool is_v = !is_q && !is_k && slot < p.hq + 2 * p.hkv;
-    const bool is_gate = !is_q && !is_k && !is_v;     // launched only with partials to add
+    const bool is_gate = !is_q && !is_k && !is_v;
     const int g = is_k ? slot - p.hq : (is_v ? slot - p.hq - p.hkv : 0);
-    const int e0 = part * EPT;
+    const int eoff = part * 4;           // element 32*i + eoff + c
     const bool valid = blk < nblk && b < p.B;
     if (blk == nblk && !is_k && !is_v) return;
     if (is_gate && !valid) return;
 
-    float x[EPT];
+    float4 x[NG];
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) x[i] = 0.f;
-    const int col0 = slot * HD + e0;     // q, k, v, gate slots are contiguous columns
+    for (int i = 0; i < NG; ++i) x[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int col0 = slot * HD + eoff;   // q, k, v, gate slots are contiguous columns
     if (valid) {
         const float* src = p.qkv + (size_t)b * p.nqkv + col0;
+        float4 q[NP > 0 ? NP : 1][NG];
 #pragma unroll
-        for (int i = 0; i < EPT; i += 4) {
-            const float4 v = *reinterpret_cast<const float4*>(src + i);
-            x[i] = v.x; x[i + 1] = v.y; x[i + 2] = v.z; x[i + 3] = v.w;
-        }
-        for (int z = 0; z < p.nparts; ++z) {
+        for (int i = 0; i < NG; ++i) x[i] = *reinterpret_cast<const float4*>(src + 32 * i);
+#pragma unroll
+        for (int z = 0; z < NP; ++z) {
             const float* ps = p.part + ((size_t)z * p.B + b) * p.nqkv + col0;
 #pragma unroll
-            for (int i = 0; i < EPT; i += 4) {
-                const float4 v = *reinterpret_cast<const float4*>(ps + i);
-                x[i] += v.x; x[i + 1] += v.y; x[i + 2] += v.z; x[i + 3] += v.w;
-            }
+            for (int i = 0; i < NG; ++i) q[z][i] = *reinterpret_cast<const float4*>(ps + 32 * i);
         }
-        if (is_gate) {          // the attention reads the gate from the projection
+#pragma unroll
+        for (int z = 0; z < NP; ++z)
+#pragma unroll
+            for (int i = 0; i < NG; ++i) {
+                x[i].x += q[z][i].x; x[i].y += q[z][i].y; x[i].z += q[z][i].z; x[i].w += q[z][i].w;
+            }
+        if (is_gate) {
             float* dst = p.qkv + (size_t)b * p.nqkv + col0;
 #pragma unroll
-            for (int i = 0; i < EPT; i += 4)
-                *reinterpret_cast<float4*>(dst + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
+            for (int i = 0; i < NG; ++i) *reinterpret_cast<float4*>(dst + 32 * i) = x[i];
             return;
         }
         if (p.bias) {
 #pragma unroll
-            for (int i = 0; i < EPT; ++i) x[i] += p.bias[col0 + i];
+            for (int i = 0; i < NG; ++i) {
+                const float4 c = *reinterpret_cast<const float4*>(p.bias + col0 + 32 * i);
+                x[i].x += c.x; x[i].y += c.y; x[i].z += c.z; x[i].w += c.w;
+            }
         }
     }
     if (is_q || is_k) {
@@ -145,60 +152,68 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs p) {
         if (gn) {
             float ss = 0.f;
 #pragma unroll
-            for (int i = 0; i < EPT; ++i) ss += x[i] * x[i];
+            for (int i = 0; i < NG; ++i) ss += x[i].x * x[i].x + x[i].y * x[i].y + x[i].z * x[i].z + x[i].w * x[i].w;
             ss += __shfl_xor(ss, 1, 64);
             ss += __shfl_xor(ss, 2, 64);
             ss += __shfl_xor(ss, 4, 64);
             const float r = 1.0f / sqrtf(ss / (float)HD + p.eps);
 #pragma unroll
-            for (int i = 0; i < EPT; ++i) x[i] = x[i] * r * gn[e0 + i];
+            for (int i = 0; i < NG; ++i) {
+                const float4 c = *reinterpret_cast<const float4*>(gn + eoff + 32 * i);
+                x[i].x = x[i].x * r * c.x; x[i].y = x[i].y * r * c.y;
+                x[i].z = x[i].z * r * c.z; x[i].w = x[i].w * r * c.w;
+            }
         }
         if (p.rope) {
-            const bool first = part < 4;          // holds the a of the pairs (a, b)
-            const int ebase = (first ? e0 : e0 - HD / 2);
-            const float2* cs = p.rope + (size_t)(valid ? b : 0) * (HD / 2) + ebase;
+            // pair (e, e + HD/2) with e = 32i + eoff + c, i < NG/2: angle index e
+            const float* cs = reinterpret_cast<const float*>(p.rope + (size_t)(valid ? b : 0) * (HD / 2));
 #pragma unroll
-            for (int i = 0; i < EPT; ++i) {
-                const float other = __shfl_xor(x[i], 4, 64);
-                const float2 c = cs[i];
-                x[i] = first ? x[i] * c.x - other * c.y : other * c.y + x[i] * c.x;
+            for (int i = 0; i < NG / 2; ++i) {
+                const float4 c01 = *reinterpret_cast<const float4*>(cs + 2 * (32 * i + eoff));
+                const float4 c23 = *reinterpret_cast<const float4*>(cs + 2 * (32 * i + eoff) + 4);
+                const float4 a = x[i], o = x[i + NG / 2];
+                x[i] = make_float4(a.x * c01.x - o.x * c01.y, a.y * c01.z - o.y * c01.w,
+                                   a.z * c23.x - o.z * c23.y, a.w * c23.z - o.w * c23.w);
+                x[i + NG / 2] = make_float4(a.x * c01.y + o.x * c01.x, a.y * c01.w + o.y * c01.z,
+                                            a.z * c23.y + o.z * c23.x, a.w * c23.w + o.w * c23.z);
             }
         }
     }
+    auto h4 = [](float4 v) { return half4{(f16)v.x, (f16)v.y, (f16)v.z, (f16)v.w}; };
     if (is_q) {
         if (valid) {
-            half8* dst = reinterpret_cast<half8*>(p.q16 + (size_t)b * p.hq * HD + slot * HD + e0);
+            f16* dst = p.q16 + (size_t)b * p.hq * HD + slot * HD + eoff;
 #pragma unroll
-            for (int i = 0; i < EPT; i += 8)
-                dst[i / 8] = half8{(f16)x[i], (f16)x[i + 1], (f16)x[i + 2], (f16)x[i + 3],
-                                   (f16)x[i + 4], (f16)x[i + 5], (f16)x[i + 6], (f16)x[i + 7]};
+            for (int i = 0; i < NG; ++i) *reinterpret_cast<half4*>(dst + 32 * i) = h4(x[i]);
         }
         return;
     }
     const size_t key = (size_t)p.S + b;            // row in the staged K/V
     if (is_k) {
         if (valid) {
-            float* dst = p.k_rows + (size_t)b * p.hkv * HD + g * HD + e0;
+            float* dst = p.k_rows + (size_t)b * p.hkv * HD + g * HD + eoff;
 #pragma unroll
-            for (int i = 0; i < EPT; i += 4)
-                *reinterpret_cast<float4*>(dst + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
+            for (int i = 0; i < NG; ++i) *reinterpret_cast<float4*>(dst + 32 * i) = x[i];
         }
-        half8* kd = reinterpret_cast<half8*>(p.k16 + ((size_t)g * p.tcap + key) * HD + e0);
+        f16* kd = p.k16 + ((size_t)g * p.tcap + key) * HD + eoff;
 #pragma unroll
-        for (int i = 0; i < EPT; i += 8)                      // zeros past B
-            kd[i / 8] = half8{(f16)x[i], (f16)x[i + 1], (f16)x[i + 2], (f16)x[i + 3],
-                              (f16)x[i + 4], (f16)x[i + 5], (f16)x[i + 6], (f16)x[i + 7]};
+        for (int i = 0; i < NG; ++i) *reinterpret_cast<half4*>(kd + 32 * i) = h4(x[i]);   // zeros past B
         return;
     }
     // v
     if (valid) {
-        float* dst = p.v_rows + (size_t)b * p.hkv * HD + g * HD + e0;
+        float* dst = p.v_rows + (size_t)b * p.hkv * HD + g * HD + eoff;
 #pragma unroll
-        for (int i = 0; i < EPT; i += 4)
-            *reinterpret_cast<float4*>(dst + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
+        for (int i = 0; i < NG; ++i) *reinterpret_cast<float4*>(dst + 32 * i) = x[i];
     }
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) vt[e0 + i][tl] = (f16)x[i];
+    for (int i = 0; i < NG; ++i) {
+        const int e = 32 * i + eoff;
+        vt[e][tl] = (f16)x[i].x;
+        vt[e + 1][tl] = (f16)x[i].y;
+        vt[e + 2][tl] = (f16)x[i].z;
+        vt[e + 3][tl] = (f16)x[i].w;
+    }
     __syncthreads();
     // row e of Vt16 gets this block's 32 keys
     for (int idx = tid; idx < HD * 32; idx += 256) {
@@ -305,19 +320,30 @@ hipError_t launch_rope_table(float2* tab, int batch, int start_pos, int half, in
     return hipGetLastError();
 }
 
+namespace {
+template <int HD>
+hipError_t launch_qkv_post_hd(const QkvPostArgs& a, dim3 grid, hipStream_t s) {
+    switch (a.nparts) {
+        case 0: hipLaunchKernelGGL((qkv_post_kernel<HD, 0>), grid, dim3(256), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((qkv_post_kernel<HD, 1>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((qkv_post_kernel<HD, 2>), grid, dim3(256), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((qkv_post_kernel<HD, 3>), grid, dim3(256), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_qkv_post(const QkvPostArgs& a, hipStream_t s) {
-    if (a.nparts > 0 && !a.part) return hipErrorInvalidValue;
+    // at most three partial slices (a four-way K split)
+    if (a.nparts < 0 || a.nparts > 3 || (a.nparts > 0 && !a.part)) return hipErrorInvalidValue;
     // the gate heads (a gated layer's second q half) take part only to get
     // their split-K partials added
     const int slots = a.hq + 2 * a.hkv + (a.gated && a.nparts > 0 ? a.hq : 0);
     const dim3 grid((a.B + 31) / 32 + 1, slots);
-    if (a.hd == 128)
-        hipLaunchKernelGGL(qkv_post_kernel<128>, grid, dim3(256), 0, s, a);
-    else if (a.hd == 64)
-        hipLaunchKernelGGL(qkv_post_kernel<64>, grid, dim3(256), 0, s, a);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
+    if (a.hd == 128) return launch_qkv_post_hd<128>(a, grid, s);
+    if (a.hd == 64) return launch_qkv_post_hd<64>(a, grid, s);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_stage_prefix(const StagePrefixArgs& a, hipStream_t s) {
