@@ -84,8 +84,12 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnPrefillArgs p
     const int lane = threadIdx.x & 63, g2 = lane >> 5, ql = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: LDS addresses stay scalar
     char* smem = smem_all + wave * NS * STAGE;
-    const int qt = gridDim.x - 1 - blockIdx.x;     // longest rows first
-    const int h = blockIdx.y;
+    // Grid (hq, query blocks): the longest rows are dispatched first, and
+    // consecutive workgroups (which the dispatcher deals out to the XCDs in
+    // turn) are different heads of one query block, so every XCD gets an
+    // equal share of the long rows.
+    const int qt = gridDim.y - 1 - blockIdx.y;
+    const int h = blockIdx.x;
     const int g = h / (p.hq / p.hkv);
     const int q0 = qt * 32;
     const int qrow = q0 + ql;                      // this lane's query token
@@ -308,7 +312,7 @@ hipError_t launch_hd(const AttnPrefillArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
         if (dev >= 0 && dev < 64) set_on[dev].store(true, std::memory_order_release);
     }
-    const dim3 grid((a.B + 31) / 32, a.hq);
+    const dim3 grid(a.hq, (a.B + 31) / 32);
     hipLaunchKernelGGL((attn_prefill_kernel<HD, CAP, NW>), grid, dim3(NW * 64), lds, s, a);
     return hipGetLastError();
 }
