@@ -367,17 +367,24 @@ __global__ __launch_bounds__(COMBINE_GROUPS * 32) void decode_attn_combine_kerne
 }
 
 // y = W x (fp16 weights times inv_scale, fp32 x) with fused epilogues; W in
-// MFMA-fragment order.  One 512-thread workgroup per 32-row block: x (RMS-
-// normed first when norm_g is set) is staged in LDS, the eight waves split
-// the 16-column blocks of K round-robin, and lane l accumulates row l % 32
-// over columns 16kb + 8*(l/32) .. +7 of each 1 KB fragment block it loads
-// (one fully coalesced load per block).  The halves of a row meet with one
-// shuffle, the waves in LDS, in a fixed order.
+// MFMA-fragment order.  x (RMS-normed first when norm_g is set) is staged
+// in LDS and the eight waves of a workgroup split the 16-column blocks of K
+// round-robin, one fully coalesced load per fragment block.
+//  RH = 1: one workgroup per 32-row block; lane l accumulates row l % 32
+//          over columns 16kb + 8*(l/32) .. +7 of each 1 KB block it loads.
+//  RH = 2: two workgroups per 32-row block, one per 16-row half (for the
+//          residual projections, whose 32-row blocks are fewer than the
+//          CUs).  One load covers that half of two consecutive blocks: lane
+//          l takes row 16h + l % 16, column half (l/16) % 2, block kb + l/32
+//          (two 256-byte runs per block).
+// Lanes of a row meet by shuffles, the waves in LDS, in a fixed order.
 constexpr int GV_WAVES = 8;
+constexpr int GV_UNROLL = 4;    // fragment loads in flight per lane (8 measured no faster)
 constexpr int GV_MAXK = 15872;  // largest K the LDS stage holds (62 KB of dynamic LDS)
 
-template <int EPI>
+template <int EPI, int RH>
 __global__ __launch_bounds__(GV_WAVES * 64) void gemv_kernel(GemvArgs p) {
+    static_assert(RH == 1 || (RH == 2 && EPI == GV_RESID), "row halves only for the residual form");
     extern __shared__ float xs[];   // [K]
     __shared__ float red[GV_WAVES][32];
     __shared__ float wsum[GV_WAVES];
@@ -396,33 +403,65 @@ __global__ __launch_bounds__(GV_WAVES * 64) void gemv_kernel(GemvArgs p) {
         for (int i = tid; i < p.K; i += GV_WAVES * 64) xs[i] = xs[i] * r * p.norm_g[i];
     }
     __syncthreads();
-    const int nb = blockIdx.x;
+    const int nb = blockIdx.x / RH, hsel = blockIdx.x % RH;
     const int kblocks = p.K >> 4;
-    const f16* wb = p.W + (size_t)nb * kblocks * 512 + lane * 8;
-    const float* xl = xs + 8 * (lane >> 5);
     float acc = 0.f;
-    int kb = wave;
-    for (; kb + 3 * GV_WAVES < kblocks; kb += 4 * GV_WAVES) {
-        half8 w[4];
+    if constexpr (RH == 1) {
+        const f16* wb = p.W + (size_t)nb * kblocks * 512 + lane * 8;
+        const float* xl = xs + 8 * (lane >> 5);
+        int kb = wave;
+        for (; kb + (GV_UNROLL - 1) * GV_WAVES < kblocks; kb += GV_UNROLL * GV_WAVES) {
+            half8 w[GV_UNROLL];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) w[u] = *reinterpret_cast<const half8*>(wb + (size_t)(kb + u * GV_WAVES) * 512);
+            for (int u = 0; u < GV_UNROLL; ++u) w[u] = *reinterpret_cast<const half8*>(wb + (size_t)(kb + u * GV_WAVES) * 512);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float* xv = xl + (kb + u * GV_WAVES) * 16;
+            for (int u = 0; u < GV_UNROLL; ++u) {
+                const float* xv = xl + (kb + u * GV_WAVES) * 16;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc += (float)w[u][j] * xv[j];
+                for (int j = 0; j < 8; ++j) acc += (float)w[u][j] * xv[j];
+            }
         }
-    }
-    for (; kb < kblocks; kb += GV_WAVES) {
-        const half8 w = *reinterpret_cast<const half8*>(wb + (size_t)kb * 512);
-        const float* xv = xl + kb * 16;
+        for (; kb < kblocks; kb += GV_WAVES) {
+            const half8 w = *reinterpret_cast<const half8*>(wb + (size_t)kb * 512);
+            const float* xv = xl + kb * 16;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc += (float)w[j] * xv[j];
+            for (int j = 0; j < 8; ++j) acc += (float)w[j] * xv[j];
+        }
+        acc += __shfl_xor(acc, 32, 64);
+        if (lane < 32) red[wave][lane] = acc;
+    } else {
+        const int khalf = (lane >> 4) & 1, kofs = lane >> 5;
+        const int fl = (lane & 15) + 16 * hsel + 32 * khalf;      // lane within the 1 KB block
+        const f16* wb = p.W + ((size_t)nb * kblocks + kofs) * 512 + fl * 8;
+        const float* xl = xs + kofs * 16 + 8 * khalf;
+        constexpr int STEP = 2 * GV_WAVES;                        // blocks per round of the waves
+        int kb = 2 * wave;                                        // this wave's pair: kb, kb + 1
+        for (; kb + (GV_UNROLL - 1) * STEP + 1 < kblocks; kb += GV_UNROLL * STEP) {
+            half8 w[GV_UNROLL];
+#pragma unroll
+            for (int u = 0; u < GV_UNROLL; ++u) w[u] = *reinterpret_cast<const half8*>(wb + (size_t)(kb + u * STEP) * 512);
+#pragma unroll
+            for (int u = 0; u < GV_UNROLL; ++u) {
+                const float* xv = xl + (kb + u * STEP) * 16;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc += (float)w[u][j] * xv[j];
+            }
+        }
+        for (; kb < kblocks; kb += STEP) {
+            if (kb + kofs < kblocks) {
+                const half8 w = *reinterpret_cast<const half8*>(wb + (size_t)kb * 512);
+                const float* xv = xl + kb * 16;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc += (float)w[j] * xv[j];
+            }
+        }
+        acc += __shfl_xor(acc, 16, 64);
+        acc += __shfl_xor(acc, 32, 64);
+        if (lane < 16) red[wave][lane] = acc;
     }
-    acc += __shfl_xor(acc, 32, 64);
-    if (lane < 32) red[wave][lane] = acc;
     __syncthreads();
-    if (tid >= 32) return;
+    constexpr int ROWS = 32 / RH;
+    if (tid >= ROWS) return;
     float y = 0.f;
 #pragma unroll
     for (int w = 0; w < GV_WAVES; ++w) y += red[w][tid];
@@ -432,7 +471,7 @@ __global__ __launch_bounds__(GV_WAVES * 64) void gemv_kernel(GemvArgs p) {
         const float other = __shfl_xor(y, 16, 64);
         if (tid < 16) p.y[nb * 16 + tid] = y / (1.0f + expf(-y)) * other;
     } else {
-        const int row = nb * 32 + tid;
+        const int row = nb * 32 + hsel * 16 + tid;
         p.y[row] = p.r[row] + y;
     }
 }
@@ -537,10 +576,13 @@ hipError_t launch_gemv(const GemvArgs& a, int epi, hipStream_t s) {
     // GV_SWIGLU: N outputs from 2N packed rows; GV_RESID: N rows
     const int rows = epi == GV_SWIGLU ? 2 * a.N : a.N;
     if (rows % 32) return hipErrorInvalidValue;
-    const dim3 grid(rows / 32);
+    const dim3 block(GV_WAVES * 64);
+    const size_t lds = a.K * sizeof(float);
     if (epi == GV_SWIGLU)
-        hipLaunchKernelGGL(gemv_kernel<GV_SWIGLU>, grid, dim3(GV_WAVES * 64), a.K * sizeof(float), s, a);
+        hipLaunchKernelGGL((gemv_kernel<GV_SWIGLU, 1>), dim3(rows / 32), block, lds, s, a);
+    else if (rows / 32 < 256)   // fewer row blocks than CUs: 16-row halves
+        hipLaunchKernelGGL((gemv_kernel<GV_RESID, 2>), dim3(rows / 16), block, lds, s, a);
     else
-        hipLaunchKernelGGL(gemv_kernel<GV_RESID>, grid, dim3(GV_WAVES * 64), a.K * sizeof(float), s, a);
+        hipLaunchKernelGGL((gemv_kernel<GV_RESID, 1>), dim3(rows / 32), block, lds, s, a);
     return hipGetLastError();
 }
