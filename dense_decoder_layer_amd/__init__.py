@@ -125,6 +125,11 @@ def layer_desc(d_model: int, n_heads: int, n_kv_heads: int, head_dim: int, d_ff:
     d.attn_softcap = softcap
     d.gated, d.has_qkv_bias, d.has_qk_norm = int(gated), int(qkv_bias), int(qk_norm)
     for k, v in extra.items():
+        if k == "rope_freq_factors" and v is not None:
+            # a host float array the descriptor points at; kept alive with it
+            arr = (ctypes.c_float * len(v))(*[float(x) for x in v])
+            d._freq_keep = arr
+            v = ctypes.cast(arr, c_void_p)
         setattr(d, k, v)
     return d
 

@@ -33,20 +33,28 @@ const char* why_unsupported(const ddl_layer_desc* d) {
     if (d->d_model <= 0 || d->n_heads <= 0 || d->n_kv_heads <= 0 || d->head_dim <= 0 ||
         d->d_ff <= 0)
         return "non-positive shape";
-    if (d->act != DDL_ACT_SWIGLU) return "FFN activation is not SwiGLU";
+    if (d->act != DDL_ACT_SWIGLU && d->act != DDL_ACT_GELU) return "unknown FFN activation";
     if (d->post_norm_eps != d->rms_eps) return "post-norm epsilon differs from rms_eps";
     if (d->v_head_dim != d->head_dim) return "v_head_dim differs from head_dim";
-    if (d->window != 0) return "sliding-window attention";
+    if (d->window < 0) return "negative sliding window";
     if (d->has_post_attn_norm || d->has_post_ffn_norm) return "post-attention/post-FFN norm";
     if (d->has_sinks) return "attention sinks";
     if (d->has_alibi) return "ALiBi";
     if (d->has_lora) return "LoRA adapter attached";
     if (d->rope_enabled) {
-        if (d->rope_layout != DDL_ROPE_NEOX) return "RoPE layout other than Neox";
-        if (d->rope_rot_dim != 0 && d->rope_rot_dim != d->head_dim) return "partial RoPE width";
-        if (d->rope_freq_factors) return "RoPE frequency factors";
-        if (d->rope_mscale != 1.0f) return "RoPE attention factor other than 1";
+        const int rd = d->rope_rot_dim == 0 ? d->head_dim : d->rope_rot_dim;
+        if (d->rope_layout != DDL_ROPE_NEOX && d->rope_layout != DDL_ROPE_NORM)
+            return "unknown RoPE layout";
+        if (rd < 2 || rd % 2 || rd > d->head_dim) return "RoPE width not even or above head_dim";
+        // a thread of the QKV post-step holds channels e and e + 32k of a head
+        if (d->rope_layout == DDL_ROPE_NEOX && (rd / 2) % 32)
+            return "Neox RoPE width not a multiple of 64";
+        if (!std::isfinite(d->rope_mscale)) return "RoPE attention factor not finite";
         if (!(d->rope_theta > 0.0)) return "RoPE theta not positive";
+        if (d->rope_freq_factors)
+            for (int i = 0; i < rd / 2; ++i)
+                if (!(d->rope_freq_factors[i] > 0.0f) || !std::isfinite(d->rope_freq_factors[i]))
+                    return "RoPE frequency factor not positive and finite";
     }
     if (d->head_dim != 64 && d->head_dim != 128) return "head_dim other than 64 or 128";
     if (d->n_heads % d->n_kv_heads != 0) return "n_heads not a multiple of n_kv_heads";
@@ -60,7 +68,7 @@ const char* why_unsupported(const ddl_layer_desc* d) {
 }
 
 struct BlobLayout {
-    size_t hdr, g_attn, g_ffn, bqkv, qn, kn, wqkv, wo, wgu, wd, total;
+    size_t hdr, g_attn, g_ffn, bqkv, qn, kn, freq, wqkv, wo, wgu, wd, total;
     int nqkv;
 };
 
@@ -80,6 +88,8 @@ void blob_layout(const ddl_layer_desc* d, BlobLayout* L) {
     L->bqkv = take(d->has_qkv_bias ? (size_t)L->nqkv * 4 : 0);
     L->qn = take(d->has_qk_norm ? (size_t)d->head_dim * 4 : 0);
     L->kn = take(d->has_qk_norm ? (size_t)d->head_dim * 4 : 0);
+    const int rd = d->rope_rot_dim == 0 ? d->head_dim : d->rope_rot_dim;
+    L->freq = take(d->rope_enabled && d->rope_freq_factors ? (size_t)(rd / 2) * 4 : 0);
     L->wqkv = take((size_t)L->nqkv * dm * 2);
     L->wo = take(dm * qw * 2);
     L->wgu = take(2 * f * dm * 2);
@@ -132,11 +142,17 @@ WsLayout ws_layout(const ddl_layer* L, int B, int S) {
     return w;
 }
 
-// Layers of one run share every shape and option the kernels specialise on.
+// Layers of one run share the shapes the workspace is laid out for; per-layer
+// options (RoPE, activation, window, softcap, extras) may differ.
 bool same_run_shape(const ddl_layer* a, const ddl_layer* b) {
     return a->d == b->d && a->hq == b->hq && a->hkv == b->hkv && a->hd == b->hd && a->f == b->f &&
-           a->gated == b->gated && a->rope_on == b->rope_on &&
-           (!a->rope_on || a->theta == b->theta);
+           a->gated == b->gated;
+}
+
+// Two rotating layers whose position tables are the same.
+bool same_rope(const ddl_layer* a, const ddl_layer* b) {
+    return a->rope_on && b->rope_on && a->theta == b->theta && a->rot_dim == b->rot_dim &&
+           a->mscale == b->mscale && a->freq_host == b->freq_host;
 }
 
 size_t elem_bytes(int dtype) { return dtype == DDL_DTYPE_BF16 ? 2 : 4; }
@@ -259,9 +275,19 @@ int ddl_layer_pack(ddl_ctx* ctx, const ddl_layer_desc* d, const ddl_layer_weight
     L->has_bias = d->has_qkv_bias;
     L->has_qk_norm = d->has_qk_norm;
     L->rope_on = d->rope_enabled;
+    L->act = d->act;
+    L->window = d->window;
     L->eps = d->rms_eps;
     L->softcap = d->attn_softcap;
     L->theta = d->rope_theta;
+    L->rope_layout = d->rope_layout;
+    L->rot_dim = d->rope_rot_dim == 0 ? d->head_dim : d->rope_rot_dim;
+    L->mscale = d->rope_mscale;
+    L->freq = nullptr;
+    if (d->rope_enabled && d->rope_freq_factors) {
+        L->freq_host.assign(d->rope_freq_factors, d->rope_freq_factors + L->rot_dim / 2);
+        L->freq = reinterpret_cast<float*>(base + B.freq);
+    }
     L->blob_bytes = B.total;
     L->hdr = reinterpret_cast<BlobHeader*>(base + B.hdr);
     L->g_attn = reinterpret_cast<float*>(base + B.g_attn);
@@ -306,6 +332,9 @@ int ddl_layer_pack(ddl_ctx* ctx, const ddl_layer_desc* d, const ddl_layer_weight
         if (!e) e = hipMemcpyAsync(L->bqkv + qw, w->bk, kw * 4, hipMemcpyDefault, s);
         if (!e) e = hipMemcpyAsync(L->bqkv + qw + kw, w->bv, kw * 4, hipMemcpyDefault, s);
     }
+    if (!e && L->freq)   // from the handle's own copy: the caller's array may go away
+        e = hipMemcpyAsync(L->freq, L->freq_host.data(), L->freq_host.size() * 4,
+                           hipMemcpyHostToDevice, s);
     if (!e && L->has_qk_norm) {
         e = hipMemcpyAsync(L->q_norm, w->q_norm, (size_t)L->hd * 4, hipMemcpyDefault, s);
         if (!e) e = hipMemcpyAsync(L->k_norm, w->k_norm, (size_t)L->hd * 4, hipMemcpyDefault, s);
@@ -391,9 +420,14 @@ int ddl_prefill_dense_stack(ddl_ctx* ctx, const float* hidden, const ddl_layer* 
     int pending = 0;                  // partials of the last down projection
 
     hipError_t e = hipSuccess;
-    if (L0->rope_on) e = launch_rope_table(rope, batch, start_pos, hd / 2, hd, L0->theta, s);
+    const ddl_layer* table_of = nullptr;   // layer whose RoPE description the table holds
     for (int l = 0; l < run && !e; ++l) {
         const ddl_layer* L = layers[l];
+        if (L->rope_on && !(table_of && same_rope(L, table_of))) {
+            e = launch_rope_table(rope, batch, start_pos, L->rot_dim, L->theta, L->freq, L->mscale, s);
+            table_of = L;
+            if (e) break;
+        }
         // the first layer reads the caller's hidden (no partials: never written)
         float* x = l == 0 ? const_cast<float*>(hidden) : hidden_out;
         // attention branch: x1 = x + wo . attn(rope(qkv(rms_norm(x))))
@@ -422,6 +456,8 @@ int ddl_prefill_dense_stack(ddl_ctx* ctx, const float* hidden, const ddl_layer* 
             q.qkv = qkv; q.nqkv = nqkv; q.part = part; q.nparts = sp_qkv - 1;
             q.bias = L->bqkv; q.q_norm = L->q_norm; q.k_norm = L->k_norm;
             q.rope = L->rope_on ? rope : nullptr;
+            q.rope_layout = L->rope_layout;
+            q.rope_half = L->rot_dim / 2;
             q.B = batch; q.S = start_pos; q.hq = hq; q.hkv = hkv; q.hd = hd; q.gated = L->gated;
             q.eps = L->eps;
             q.q16 = q16; q.k_rows = k_rows[l]; q.v_rows = v_rows[l];
@@ -437,6 +473,7 @@ int ddl_prefill_dense_stack(ddl_ctx* ctx, const float* hidden, const ddl_layer* 
             a.o16 = o16;
             a.B = batch; a.S = start_pos; a.hq = hq; a.hkv = hkv; a.hd = hd;
             a.softcap = L->softcap;
+            a.window = L->window;
             ProbeScope p(ctx, DDL_K_ATTN_PREFILL, s);
             e = launch_attn_prefill(a, s);
         }
@@ -461,7 +498,7 @@ int ddl_prefill_dense_stack(ddl_ctx* ctx, const float* hidden, const ddl_layer* 
             g.inv_scale = &L->hdr->inv_scale[MAT_GU];
             g.H = a16; g.ldh = f;
             ProbeScope p(ctx, DDL_K_GEMM_GATE_UP, s);
-            e = launch_gemm(g, EPI_SWIGLU, 1, s);
+            e = launch_gemm(g, L->act == DDL_ACT_GELU ? EPI_GEGLU : EPI_SWIGLU, 1, s);
         }
         if (!e) {
             GemmArgs g{};
@@ -595,6 +632,9 @@ int ddl_attn_layer(ddl_ctx* ctx, ddl_mirror* m, int host_rows, const float* q, c
         return fail(DDL_DECLINED, "query-head group size not served");
     if (!gemv_shape_ok(L->d) || !gemv_shape_ok(L->f) || !gemv_shape_ok(L->hq * L->hd))
         return fail(DDL_DECLINED, "GEMV width not served");
+    // "frink-models 0.38.0 src/decoder/device_attention.rs",
+    // device_attention_shape_ok: no sliding window on this path
+    if (L->window != 0) return fail(DDL_DECLINED, "sliding-window layer");
     if (!(softcap >= 0.0f)) return fail(DDL_ERR_INVALID, "negative softcap");
     const AttnWs W = attn_ws(L);
     if (!workspace || workspace_bytes < W.total)
@@ -637,6 +677,7 @@ int ddl_attn_layer(ddl_ctx* ctx, ddl_mirror* m, int host_rows, const float* q, c
         g.W = L->wgu; g.K = L->d; g.N = L->f;
         g.inv_scale = &L->hdr->inv_scale[MAT_GU];
         g.x = x1; g.norm_g = L->g_ffn; g.eps = L->eps; g.y = a;
+        g.gelu = L->act == DDL_ACT_GELU;
         ProbeScope p(ctx, DDL_K_GEMV_GATE_UP, s);
         e = launch_gemv(g, GV_SWIGLU, s);
     }

@@ -23,7 +23,10 @@
 // so rescaling O is rare.  Tiles wholly above the wave's last query are not
 // visited; only tiles on the diagonal or past the last key apply the causal
 // mask, and masked scores are -inf and contribute exact zeros, so a token's
-// outputs do not depend on later tokens' values.
+// outputs do not depend on later tokens' values.  With a sliding window W
+// (cuda_prefill_layer's `window`) the token at position p sees keys
+// p-W+1 .. p: tiles wholly below the block's first window are not visited and
+// the tiles across its lower edge are masked too.
 #include "common.h"
 #include "internal.h"
 
@@ -97,8 +100,15 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnPrefillArgs p
     const int nkeys = p.S + p.B;
     const int kv_end = min(p.S + q0 + 32, nkeys);  // keys the wave can see
     const int ntiles = (kv_end + KT - 1) / KT;
-    const int my_n = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;   // this wave's tiles
-    auto tile_of = [&](int i) { return wave + i * NW; };
+    // first key of the block's first query's window; tiles before its tile
+    // hold no visible key for any query of the block
+    const int win_lo = p.window > 0 ? max(p.S + q0 - p.window + 1, 0) : 0;
+    const int t0 = win_lo / KT;
+    const int my_n = ntiles - t0 > wave ? (ntiles - t0 - wave + NW - 1) / NW : 0;   // this wave's tiles
+    auto tile_of = [&](int i) { return t0 + wave + i * NW; };
+    // keys below this bound are outside the last query's window: a tile
+    // starting below it may hold keys outside some query's window
+    const int win_edge = p.window > 0 ? p.S + q0 + 32 - p.window : -1;
     const float LOG2E = 1.4426950408889634f;
     const float scale = 1.0f / sqrtf((float)HD);
     // exp2-domain logit: c * s, or capl * tanh(s * ic) with a softcap
@@ -185,11 +195,12 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnPrefillArgs p
         }
         // only a tile that reaches past the block's first query or past the
         // last key needs the mask (a wave-uniform test)
-        if (k0 + KT - 1 > p.S + q0 || k0 + KT > nkeys) {
+        if (k0 + KT - 1 > p.S + q0 || k0 + KT > nkeys || k0 < win_edge) {
+            const int klo = p.window > 0 ? qpos - p.window : -1;   // keys <= klo are outside the window
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int kpos = k0 + 8 * (e >> 2) + 4 * g2 + (e & 3);
-                sv[e] = ((kpos <= qpos) & (kpos < nkeys)) ? sv[e] : -INFINITY;
+                sv[e] = ((kpos <= qpos) & (kpos < nkeys) & (kpos > klo)) ? sv[e] : -INFINITY;
             }
         }
         float tmax = sv[0];
@@ -261,8 +272,11 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnPrefillArgs p
     if (wave > 0) return;
     for (int w = 1; w < NW; ++w) {
         const float mo = mbuf[(w - 1) * 32 + ql], lo = lbuf[(w - 1) * 32 + ql];
-        const float mn = fmaxf(m, mo);              // finite: tile 0 holds key 0
-        const float a = __builtin_amdgcn_exp2f(m - mn), b = __builtin_amdgcn_exp2f(mo - mn);
+        // finite: the tile holding a query's own key is visited by one of
+        // the waves; a wave that saw no visible key has m = -inf, l = 0, O = 0
+        const float mn = fmaxf(m, mo);
+        const float a = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+        const float b = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
         l = l * a + lo * b;
         m = mn;
 #pragma unroll
@@ -319,7 +333,7 @@ hipError_t launch_hd(const AttnPrefillArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s) {
-    if (a.tcap % 32 || a.tcap < a.S + a.B) return hipErrorInvalidValue;
+    if (a.tcap % 32 || a.tcap < a.S + a.B || a.window < 0) return hipErrorInvalidValue;
     const bool cap = a.softcap > 0.f;
     if (a.hd == 128) return cap ? launch_hd<128, true>(a, s) : launch_hd<128, false>(a, s);
     if (a.hd == 64) return cap ? launch_hd<64, true>(a, s) : launch_hd<64, false>(a, s);

@@ -469,7 +469,9 @@ __global__ __launch_bounds__(GV_WAVES * 64) void gemv_kernel(GemvArgs p) {
     if constexpr (EPI == GV_SWIGLU) {
         // rows 32nb + t: t < 16 gate, t >= 16 up, of output 16nb + t % 16
         const float other = __shfl_xor(y, 16, 64);
-        if (tid < 16) p.y[nb * 16 + tid] = y / (1.0f + expf(-y)) * other;
+        const float act = p.gelu ? 0.5f * y * (1.0f + erff(y * 0.7071067811865476f))
+                                 : y / (1.0f + expf(-y));
+        if (tid < 16) p.y[nb * 16 + tid] = act * other;
     } else {
         const int row = nb * 32 + hsel * 16 + tid;
         p.y[row] = p.r[row] + y;

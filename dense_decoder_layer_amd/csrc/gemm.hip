@@ -10,6 +10,9 @@
 //   EPI_RESID   C = R + acc (wo and down projections plus the residual)
 //   EPI_SWIGLU  W rows are gate/up interleaved in 16-row blocks; store
 //               fp16 silu(gate) * up into H[M][N/2]
+//   EPI_GEGLU   the same with the exact GELU, gate * Phi(gate), in place of
+//               silu (the GELU-gated FFN of "frink-models 0.29.0
+//               src/decoder/cuda_prefill.rs", try_cuda_prefill_dense_stack)
 //
 // Design (gfx950, v_mfma_f32_32x32x16_f16):
 //  * W is stored in MFMA-fragment order (see the packing kernels): the
@@ -74,7 +77,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, floatx16 (&acc)[MI][
     const float sc = *p.inv_scale;
     const int rbase = row0 + 4 * (lane >> 5);
     const int cl = lane & 31;
-    if constexpr (EPI == EPI_SWIGLU) {
+    if constexpr (EPI == EPI_SWIGLU || EPI == EPI_GEGLU) {
         // a 32-column tile holds gate block 2q (lanes 0..15 of the columns)
         // and up block 2q+1 (lanes 16..31) of the same 16 outputs
 #pragma unroll
@@ -87,7 +90,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, floatx16 (&acc)[MI][
                 for (int e = 0; e < 16; ++e) {
                     const float v = acc[i][j][e] * sc;
                     const float other = __shfl_xor(v, 16, 64);   // lane l^16 holds the partner
-                    a[e] = v / (1.0f + expf(-v)) * other;
+                    const float act = EPI == EPI_GEGLU ? 0.5f * v * (1.0f + erff(v * 0.7071067811865476f))
+                                                       : v / (1.0f + expf(-v));
+                    a[e] = act * other;
                 }
                 if (cl < 16) {
 #pragma unroll
@@ -309,7 +314,7 @@ int split_count(int tiles, int slots, int nk) {
 
 Plan gemm_plan(int M, int N, int K, int epi) {
     const int nk = K / BK;
-    if (epi == EPI_SWIGLU) return {N % 256 == 0 && M > 64 ? T128x256 : T128x128, 1};
+    if (epi == EPI_SWIGLU || epi == EPI_GEGLU) return {N % 256 == 0 && M > 64 ? T128x256 : T128x128, 1};
     if (epi == EPI_F32 && N % 256 == 0 && M > 64)
         return {T128x256, split_count(((M + 127) / 128) * (N / 256), 256, nk)};
     const int splits = split_count(((M + 63) / 64) * (N / 128), 768, nk);
@@ -326,13 +331,17 @@ int gemm_splits(int M, int N, int K, int epi) {
 
 hipError_t launch_gemm(const GemmArgs& a, int epi, int splits, hipStream_t s) {
     if (!gemm_shape_ok(a.M, a.N, a.K, epi)) return hipErrorInvalidValue;
-    if (splits < 1 || (a.K / BK) % splits || (splits > 1 && (!a.P || epi == EPI_SWIGLU)))
+    if (splits < 1 || (a.K / BK) % splits ||
+        (splits > 1 && (!a.P || epi == EPI_SWIGLU || epi == EPI_GEGLU)))
         return hipErrorInvalidValue;
     const Tile t = gemm_plan(a.M, a.N, a.K, epi).tile;
     switch (epi) {
         case EPI_SWIGLU:
             if (t == T128x256) return launch_nk<128, 32, 1, 8, 3, EPI_SWIGLU>(a, 1, s);
             return launch_nk<128, 32, 1, 4, 4, EPI_SWIGLU>(a, 1, s);
+        case EPI_GEGLU:
+            if (t == T128x256) return launch_nk<128, 32, 1, 8, 3, EPI_GEGLU>(a, 1, s);
+            return launch_nk<128, 32, 1, 4, 4, EPI_GEGLU>(a, 1, s);
         case EPI_F32:
             if (t == T128x256) return launch_nk<128, 32, 1, 8, 3, EPI_F32>(a, splits, s);
             return launch_nk<64, 32, 1, 4, 4, EPI_F32>(a, splits, s);

@@ -63,8 +63,14 @@ static_assert(sizeof(BlobHeader) == 256, "header is one 256-byte line");
 struct ddl_layer {
     int d, hq, hkv, hd, f, nqkv;
     int gated, has_bias, has_qk_norm, rope_on;
+    int act;                     // DDL_ACT_SWIGLU or DDL_ACT_GELU (gated GELU)
+    int window;                  // sliding window (keys per query), 0 = none
     float eps, softcap;
     double theta;
+    int rope_layout, rot_dim;    // DDL_ROPE_*, rotated channels per head
+    float mscale;                // attention factor on the rotated channels
+    std::vector<float> freq_host;   // frequency factors (empty: none), host copy
+    float* freq;                 // the same in the blob, [rot_dim/2] or null
     size_t blob_bytes;
     BlobHeader* hdr;
     float *g_attn, *g_ffn, *bqkv, *q_norm, *k_norm;
@@ -79,7 +85,7 @@ struct ddl_mirror {
 
 // ---- launchers (each enqueues on `s`; return hipGetLastError()) ----------
 
-enum { EPI_F32 = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+enum { EPI_F32 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_GEGLU = 3 };
 
 struct GemmArgs {
     const f16* A; int lda;      // [M][K]
@@ -88,7 +94,7 @@ struct GemmArgs {
     const float* inv_scale;     // device scalar, multiplies the accumulator
     float* C; int ldc;          // EPI_F32, EPI_RESID output
     const float* R; int ldr;    // EPI_RESID residual input (may alias C)
-    f16* H; int ldh;            // EPI_SWIGLU output [M][N/2]
+    f16* H; int ldh;            // EPI_SWIGLU / EPI_GEGLU output [M][N/2]
     // Split-K (EPI_F32, EPI_RESID): slice 0 of the K range applies the
     // epilogue to C; slice z > 0 stores its raw scaled sum to
     // P + (z - 1) * M * ldc, [M][ldc], which the consumer adds in.
@@ -108,8 +114,10 @@ int gemm_splits(int M, int N, int K, int epi);
 hipError_t launch_rmsnorm_f16(float* x, const float* g, f16* h, int rows, int d, float eps,
                               const float* part, int nparts, hipStream_t s);
 
-hipError_t launch_rope_table(float2* tab, int batch, int start_pos, int half, int rot_dim,
-                             double theta, hipStream_t s);
+// tab[b][i] = m * (cos, sin) of (start_pos + b) * theta^(-2i/rot_dim) / freq[i]
+// for the rot_dim/2 rotated pairs i (freq may be null: factors of 1).
+hipError_t launch_rope_table(float2* tab, int batch, int start_pos, int rot_dim, double theta,
+                             const float* freq, float mscale, hipStream_t s);
 
 // Staged fp16 K/V of one layer for the attention kernel, tcap rows per KV
 // head (a multiple of 32, at least S + 32*(ceil(B/32)+1)):
@@ -121,7 +129,10 @@ struct QkvPostArgs {
                                         // gate columns get the partials added in place)
     const float* bias;                  // [nqkv] or null
     const float* q_norm; const float* k_norm;   // [hd] or null
-    const float2* rope;                 // [B][hd/2] or null
+    const float2* rope;                 // [B][rope_half] (launch_rope_table) or null
+    int rope_layout;                    // DDL_ROPE_NEOX: pairs (i, i + rope_half);
+                                        // DDL_ROPE_NORM: pairs (2i, 2i + 1); i < rope_half
+    int rope_half;                      // rotated pairs per head (rot_dim / 2)
     int B, S, hq, hkv, hd, gated; float eps;
     f16* q16;                           // [B][hq*hd]
     float* k_rows; float* v_rows;       // [B][hkv*hd]
@@ -143,6 +154,7 @@ struct AttnPrefillArgs {
     f16* o16;                            // [B][hq*hd]
     int B, S, hq, hkv, hd;
     float softcap;
+    int window;                          // > 0: token at position p sees keys p-window+1 .. p
 };
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s);
 
@@ -192,6 +204,7 @@ struct GemvArgs {
     const float* norm_g; float eps;   // RMS-norm x first when norm_g != null
     const float* r;              // [N] residual (GV_RESID)
     float* y;                    // [N]
+    int gelu;                    // GV_SWIGLU: gelu(gate) * up instead of silu(gate) * up
 };
 bool gemv_shape_ok(int K);
 hipError_t launch_gemv(const GemvArgs& a, int epi, hipStream_t s);

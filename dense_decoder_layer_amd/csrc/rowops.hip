@@ -18,37 +18,39 @@ namespace {
 // normalised and stored as fp16.
 constexpr int RMS_V4 = 4;   // float4s per thread: 256 * 4 * 4 = 4096 columns
 
-// With nparts > 0 the split-K partials of the GEMM that produced x are
-// added first (in slice order) and the sum is written back to x.
+// With NP > 0 the split-K partials of the GEMM that produced x are added
+// first (in slice order) and the sum is written back to x.  The partial
+// count is a template parameter so every load of the row is issued before
+// the first add (one memory round trip, not one per slice).
+template <int NP>
 __global__ __launch_bounds__(256) void rmsnorm_f16_kernel(float* __restrict__ x,
                                                           const float* __restrict__ g,
                                                           f16* __restrict__ h, int d, float eps,
                                                           const float* __restrict__ part,
-                                                          int nparts, size_t pstride) {
+                                                          size_t pstride) {
     __shared__ float red[4];
     const size_t row = blockIdx.x;
     float4* xr = reinterpret_cast<float4*>(x + row * d);
     const float4* gr = reinterpret_cast<const float4*>(g);
     const int n4 = d >> 2;
-    float4 v[RMS_V4], w[RMS_V4];
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 v[RMS_V4], w[RMS_V4], q[NP > 0 ? NP : 1][RMS_V4];
 #pragma unroll
     for (int k = 0; k < RMS_V4; ++k) {
         const int i = threadIdx.x + k * 256;
-        v[k] = i < n4 ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-        w[k] = i < n4 ? gr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[k] = i < n4 ? xr[i] : zero;
+        w[k] = i < n4 ? gr[i] : zero;
+#pragma unroll
+        for (int z = 0; z < NP; ++z)
+            q[z][k] = i < n4 ? reinterpret_cast<const float4*>(part + z * pstride + row * d)[i] : zero;
     }
-    if (nparts > 0) {
-        for (int z = 0; z < nparts; ++z) {
-            const float4* pr = reinterpret_cast<const float4*>(part + z * pstride + row * d);
+    if constexpr (NP > 0) {
+#pragma unroll
+        for (int z = 0; z < NP; ++z)
 #pragma unroll
             for (int k = 0; k < RMS_V4; ++k) {
-                const int i = threadIdx.x + k * 256;
-                if (i < n4) {
-                    const float4 q = pr[i];
-                    v[k].x += q.x; v[k].y += q.y; v[k].z += q.z; v[k].w += q.w;
-                }
+                v[k].x += q[z][k].x; v[k].y += q[z][k].y; v[k].z += q[z][k].z; v[k].w += q[z][k].w;
             }
-        }
 #pragma unroll
         for (int k = 0; k < RMS_V4; ++k) {
             const int i = threadIdx.x + k * 256;
@@ -70,16 +72,21 @@ __global__ __launch_bounds__(256) void rmsnorm_f16_kernel(float* __restrict__ x,
     }
 }
 
-// cos/sin of pair i at position start_pos + b, angle computed in fp64:
-// (start_pos + b) * theta^(-2i/rot_dim).
-__global__ void rope_table_kernel(float2* tab, int batch, int start_pos, int half, int rot_dim,
-                                  double theta) {
+// cos/sin of rotated pair i at position start_pos + b, times the attention
+// factor m; the angle is computed in fp64: (start_pos + b) * theta^(-2i/rot_dim)
+// divided by the pair's frequency factor when the layer has them
+// ("frink-models 0.29.0 src/decoder/cuda_prefill.rs", cuda_prefill_layer:
+// theta, freq_factors, rot_dim, mscale).
+__global__ void rope_table_kernel(float2* tab, int batch, int start_pos, int rot_dim,
+                                  double theta, const float* freq, float mscale) {
+    const int half = rot_dim / 2;
     const int idx = blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= batch * half) return;
     const int b = idx / half, i = idx - b * half;
-    const double inv = pow(theta, -2.0 * (double)i / (double)rot_dim);
+    double inv = pow(theta, -2.0 * (double)i / (double)rot_dim);
+    if (freq) inv /= (double)freq[i];
     const double ang = (double)(start_pos + b) * inv;
-    tab[idx] = make_float2((float)cos(ang), (float)sin(ang));
+    tab[idx] = make_float2((float)(mscale * cos(ang)), (float)(mscale * sin(ang)));
 }
 
 // One 256-thread block per (block of 32 tokens, head slot).  Slots: [0, hq)
@@ -165,17 +172,46 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs p) {
             }
         }
         if (p.rope) {
-            // pair (e, e + HD/2) with e = 32i + eoff + c, i < NG/2: angle index e
-            const float* cs = reinterpret_cast<const float*>(p.rope + (size_t)(valid ? b : 0) * (HD / 2));
+            const float* cs = reinterpret_cast<const float*>(p.rope + (size_t)(valid ? b : 0) * p.rope_half);
+            if (p.rope_layout == DDL_ROPE_NEOX) {
+                // pair (e, e + rope_half), rope_half = 32k: element e = 32i + eoff + c
+                // (i < k) pairs with x[i + k] of the same thread; angle index e
+                const int k = p.rope_half / 32;
 #pragma unroll
-            for (int i = 0; i < NG / 2; ++i) {
-                const float4 c01 = *reinterpret_cast<const float4*>(cs + 2 * (32 * i + eoff));
-                const float4 c23 = *reinterpret_cast<const float4*>(cs + 2 * (32 * i + eoff) + 4);
-                const float4 a = x[i], o = x[i + NG / 2];
-                x[i] = make_float4(a.x * c01.x - o.x * c01.y, a.y * c01.z - o.y * c01.w,
-                                   a.z * c23.x - o.z * c23.y, a.w * c23.z - o.w * c23.w);
-                x[i + NG / 2] = make_float4(a.x * c01.y + o.x * c01.x, a.y * c01.w + o.y * c01.z,
-                                            a.z * c23.y + o.z * c23.x, a.w * c23.w + o.w * c23.z);
+                for (int i = 0; i < NG / 2; ++i) {
+                    if (i >= k) break;
+                    const float4 c01 = *reinterpret_cast<const float4*>(cs + 2 * (32 * i + eoff));
+                    const float4 c23 = *reinterpret_cast<const float4*>(cs + 2 * (32 * i + eoff) + 4);
+                    const float4 a = x[i];
+#pragma unroll
+                    for (int j = 0; j < NG; ++j) {       // x[i + k], with k not a compile-time value
+                        if (j != i + k) continue;
+                        const float4 o = x[j];
+                        x[i] = make_float4(a.x * c01.x - o.x * c01.y, a.y * c01.z - o.y * c01.w,
+                                           a.z * c23.x - o.z * c23.y, a.w * c23.z - o.w * c23.w);
+                        x[j] = make_float4(a.x * c01.y + o.x * c01.x, a.y * c01.w + o.y * c01.z,
+                                           a.z * c23.y + o.z * c23.x, a.w * c23.w + o.w * c23.z);
+                    }
+                }
+            } else {
+                // adjacent pairs (2j, 2j + 1) = (x, y) and (z, w) of a float4; pair
+                // j = e/2 rotates while j < rope_half
+#pragma unroll
+                for (int i = 0; i < NG; ++i) {
+                    const int j0 = (32 * i + eoff) >> 1;
+                    if (j0 < p.rope_half) {
+                        const float2 c0 = *reinterpret_cast<const float2*>(cs + 2 * j0);
+                        const float a = x[i].x, o = x[i].y;
+                        x[i].x = a * c0.x - o * c0.y;
+                        x[i].y = a * c0.y + o * c0.x;
+                    }
+                    if (j0 + 1 < p.rope_half) {
+                        const float2 c1 = *reinterpret_cast<const float2*>(cs + 2 * (j0 + 1));
+                        const float a = x[i].z, o = x[i].w;
+                        x[i].z = a * c1.x - o * c1.y;
+                        x[i].w = a * c1.y + o * c1.x;
+                    }
+                }
             }
         }
     }
@@ -306,17 +342,24 @@ int grid_for(size_t n) {
 
 hipError_t launch_rmsnorm_f16(float* x, const float* g, f16* h, int rows, int d, float eps,
                               const float* part, int nparts, hipStream_t s) {
-    if (d % 4 || d > 256 * 4 * RMS_V4 || (nparts > 0 && !part)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3(rows), dim3(256), 0, s, x, g, h, d, eps, part,
-                       nparts, (size_t)rows * d);
+    if (d % 4 || d > 256 * 4 * RMS_V4 || nparts < 0 || nparts > 3 || (nparts > 0 && !part))
+        return hipErrorInvalidValue;
+    const size_t ps = (size_t)rows * d;
+    switch (nparts) {
+        case 0: hipLaunchKernelGGL(rmsnorm_f16_kernel<0>, dim3(rows), dim3(256), 0, s, x, g, h, d, eps, part, ps); break;
+        case 1: hipLaunchKernelGGL(rmsnorm_f16_kernel<1>, dim3(rows), dim3(256), 0, s, x, g, h, d, eps, part, ps); break;
+        case 2: hipLaunchKernelGGL(rmsnorm_f16_kernel<2>, dim3(rows), dim3(256), 0, s, x, g, h, d, eps, part, ps); break;
+        case 3: hipLaunchKernelGGL(rmsnorm_f16_kernel<3>, dim3(rows), dim3(256), 0, s, x, g, h, d, eps, part, ps); break;
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_rope_table(float2* tab, int batch, int start_pos, int half, int rot_dim,
-                             double theta, hipStream_t s) {
-    const int n = batch * half;
+hipError_t launch_rope_table(float2* tab, int batch, int start_pos, int rot_dim, double theta,
+                             const float* freq, float mscale, hipStream_t s) {
+    if (rot_dim < 2 || rot_dim % 2) return hipErrorInvalidValue;
+    const int n = batch * (rot_dim / 2);
     hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s, tab, batch,
-                       start_pos, half, rot_dim, theta);
+                       start_pos, rot_dim, theta, freq, mscale);
     return hipGetLastError();
 }
 
@@ -337,6 +380,12 @@ hipError_t launch_qkv_post_hd(const QkvPostArgs& a, dim3 grid, hipStream_t s) {
 hipError_t launch_qkv_post(const QkvPostArgs& a, hipStream_t s) {
     // at most three partial slices (a four-way K split)
     if (a.nparts < 0 || a.nparts > 3 || (a.nparts > 0 && !a.part)) return hipErrorInvalidValue;
+    // rotated pairs: Neox needs rope_half a multiple of 32 (a thread holds
+    // both channels of its pairs), Norm any count up to hd/2
+    if (a.rope && (a.rope_half < 1 || 2 * a.rope_half > a.hd ||
+                   (a.rope_layout == DDL_ROPE_NEOX && a.rope_half % 32) ||
+                   (a.rope_layout != DDL_ROPE_NEOX && a.rope_layout != DDL_ROPE_NORM)))
+        return hipErrorInvalidValue;
     // the gate heads (a gated layer's second q half) take part only to get
     // their split-K partials added
     const int slots = a.hq + 2 * a.hkv + (a.gated && a.nparts > 0 ? a.hq : 0);

@@ -8,19 +8,26 @@ from typing import Iterable, List, Mapping, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (Ctx, Layer, ddl_prefill_dense_stack, ddl_workspace_bytes, layer_desc,
-               pack_layer_from_host)
+from . import (DDL_ACT_GELU, DDL_ACT_SWIGLU, DDL_ROPE_NEOX, DDL_ROPE_NORM, Ctx, Layer,
+               ddl_prefill_dense_stack, ddl_workspace_bytes, layer_desc, pack_layer_from_host)
 
 
 def desc_for(cfg):
     """ddl_layer_desc of a layer shaped like ``cfg`` (any object with the
-    fields d_model, n_heads, n_kv_heads, head_dim, d_ff, rms_eps, rope_theta,
-    softcap, gated, qkv_bias, qk_norm)."""
+    fields d_model, n_heads, n_kv_heads, head_dim, d_ff, rms_eps and,
+    optionally, rope_theta, rope_layout, rope_rot_dim, rope_mscale,
+    rope_freq_factors, softcap, gated, qkv_bias, qk_norm, ffn_act, window)."""
+    layout = {"neox": DDL_ROPE_NEOX, "norm": DDL_ROPE_NORM}[getattr(cfg, "rope_layout", "neox")]
+    act = {"swiglu": DDL_ACT_SWIGLU, "geglu": DDL_ACT_GELU}[getattr(cfg, "ffn_act", "swiglu")]
     return layer_desc(cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.d_ff,
                       rms_eps=cfg.rms_eps, rope_theta=getattr(cfg, "rope_theta", None),
                       softcap=getattr(cfg, "softcap", 0.0), gated=getattr(cfg, "gated", False),
                       qkv_bias=getattr(cfg, "qkv_bias", False),
-                      qk_norm=getattr(cfg, "qk_norm", False))
+                      qk_norm=getattr(cfg, "qk_norm", False),
+                      rope_layout=layout, rope_rot_dim=getattr(cfg, "rope_rot_dim", 0),
+                      rope_mscale=getattr(cfg, "rope_mscale", 1.0),
+                      rope_freq_factors=getattr(cfg, "rope_freq_factors", None),
+                      act=act, window=getattr(cfg, "window", 0))
 
 
 class DeviceStack:

@@ -43,7 +43,11 @@ pages leave open is a stated reading (the design doc lists them all):
   max-subtracted softmax.
 * The output gate multiplies the attention output element-wise by
   ``sigmoid(gate)``; a gated ``wq`` is ``[q rows ; gate rows]``.
-* SwiGLU is ``silu(h Wg^T) * (h Wu^T)`` with ``silu(z) = z / (1 + e^-z)``.
+* SwiGLU is ``silu(h Wg^T) * (h Wu^T)`` with ``silu(z) = z / (1 + e^-z)``;
+  the GELU-gated FFN puts the exact GELU ``z * Phi(z)`` (normal CDF, erf
+  form) in place of silu.
+* A sliding window ``W`` lets the token at position ``p`` see keys
+  ``p-W+1 .. p`` (its own key and the ``W-1`` before it).
 * The stack returns the last layer's residual stream, with no final norm.
 * The decode layer attends over the cached rows plus its own new row.
 
@@ -56,7 +60,7 @@ from typing import Iterable, List, Mapping, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
-    "rms_norm", "rope_angles", "apply_rope", "causal_gqa_attention", "silu",
+    "rms_norm", "rope_angles", "apply_rope", "causal_gqa_attention", "silu", "gelu",
     "swiglu_ffn", "project_qkv", "dense_layer", "prefill_dense_stack",
     "attn_layer", "kv_head_of",
 ]
@@ -135,7 +139,7 @@ def apply_rope(x, positions, theta: float, layout: str = "neox",
 
 
 def causal_gqa_attention(q, k_all, v_all, start_pos: int, softcap: float = 0.0,
-                         gate=None) -> np.ndarray:
+                         gate=None, window: int = 0) -> np.ndarray:
     """Causal GQA attention of ``B`` new tokens over ``start_pos`` cached
     rows followed by the new rows.
 
@@ -145,8 +149,9 @@ def causal_gqa_attention(q, k_all, v_all, start_pos: int, softcap: float = 0.0,
 
     cuda_prefill.rs (0.29.0), ``cuda_prefill_layer``: the attention
     parameters -- head counts, scale 1/sqrt(head_dim), optional softcap, the
-    cache prefix, ``start_pos``; device_attention.rs (0.38.0),
-    ``device_attention_layer``: the gate is applied to the attention output.
+    cache prefix, ``start_pos``, the sliding ``window``; device_attention.rs
+    (0.38.0), ``device_attention_layer``: the gate is applied to the
+    attention output.
     """
     q, k_all, v_all = _f64(q), _f64(k_all), _f64(v_all)
     B, Hq, hd = q.shape
@@ -154,7 +159,10 @@ def causal_gqa_attention(q, k_all, v_all, start_pos: int, softcap: float = 0.0,
     assert T == start_pos + B
     scale = 1.0 / np.sqrt(hd)
     # key j is visible to token b iff j <= start_pos + b
-    visible = np.arange(T)[None, :] <= (start_pos + np.arange(B))[:, None]
+    pos = (start_pos + np.arange(B))[:, None]
+    visible = np.arange(T)[None, :] <= pos
+    if window:
+        visible &= np.arange(T)[None, :] > pos - window
     o = np.empty((B, Hq, hd), F64)
     for h in range(Hq):
         g = kv_head_of(h, Hq, Hkv)
@@ -176,15 +184,25 @@ def silu(z) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
-def swiglu_ffn(h2, wg, wu, wd) -> np.ndarray:
-    """``(silu(h2 Wg^T) * (h2 Wu^T)) Wd^T``.
+def gelu(z) -> np.ndarray:
+    """Exact GELU, ``z * Phi(z)`` with the standard normal CDF."""
+    from scipy.special import erf
+    z = _f64(z)
+    return 0.5 * z * (1.0 + erf(z / np.sqrt(2.0)))
+
+
+def swiglu_ffn(h2, wg, wu, wd, act: str = "swiglu") -> np.ndarray:
+    """``(act(h2 Wg^T) * (h2 Wu^T)) Wd^T`` with ``act`` silu (SwiGLU) or
+    GELU (the GELU-gated FFN).
 
     cuda_prefill.rs (0.29.0), ``try_cuda_prefill_dense_stack``: the fused
-    body's activation is SwiGLU; fused_layer.rs (0.49.0): one dense expert's
-    gate, up and down.
+    body's activation is SwiGLU, the other gated activation is GELU;
+    fused_layer.rs (0.49.0): one dense expert's gate, up and down.
     """
     h2 = _f64(h2)
-    return (silu(h2 @ _f64(wg).T) * (h2 @ _f64(wu).T)) @ _f64(wd).T
+    g = h2 @ _f64(wg).T
+    a = gelu(g) if act == "geglu" else silu(g)
+    return (a * (h2 @ _f64(wu).T)) @ _f64(wd).T
 
 
 def project_qkv(h, w: Mapping[str, np.ndarray], spec, positions):
@@ -213,9 +231,12 @@ def project_qkv(h, w: Mapping[str, np.ndarray], spec, positions):
         q = rms_norm(q, w["q_norm"], spec.rms_eps)
         k = rms_norm(k, w["k_norm"], spec.rms_eps)
     if getattr(spec, "rope_theta", None):
-        lay = getattr(spec, "rope_layout", "neox")
-        q = apply_rope(q, positions, spec.rope_theta, lay)
-        k = apply_rope(k, positions, spec.rope_theta, lay)
+        rope = dict(layout=getattr(spec, "rope_layout", "neox"),
+                    rot_dim=getattr(spec, "rope_rot_dim", 0) or None,
+                    freq_factors=getattr(spec, "rope_freq_factors", None),
+                    mscale=getattr(spec, "rope_mscale", 1.0))
+        q = apply_rope(q, positions, spec.rope_theta, **rope)
+        k = apply_rope(k, positions, spec.rope_theta, **rope)
     return q, gate, k, v
 
 
@@ -244,10 +265,11 @@ def dense_layer(x, w: Mapping[str, np.ndarray], spec, start_pos: int,
     else:
         k_all, v_all = k, v
     o = causal_gqa_attention(q, k_all, v_all, start_pos,
-                             getattr(spec, "softcap", 0.0), gate)
+                             getattr(spec, "softcap", 0.0), gate,
+                             getattr(spec, "window", 0))
     x1 = x + o.reshape(B, -1) @ _f64(w["wo"]).T
     h2 = rms_norm(x1, w["g_ffn"], spec.rms_eps)
-    x2 = x1 + swiglu_ffn(h2, w["wg"], w["wu"], w["wd"])
+    x2 = x1 + swiglu_ffn(h2, w["wg"], w["wu"], w["wd"], getattr(spec, "ffn_act", "swiglu"))
     return x2, k.reshape(B, Hkv * hd), v.reshape(B, Hkv * hd)
 
 
@@ -296,4 +318,5 @@ def attn_layer(q, k, v, gate, cache_k, cache_v, rows: int,
                              getattr(spec, "softcap", 0.0), g)
     x1 = _f64(residual) + _f64(w["wo"]) @ o.reshape(-1)
     h2 = rms_norm(x1, w["g_ffn"], spec.rms_eps)
-    return x1 + swiglu_ffn(h2[None], w["wg"], w["wu"], w["wd"])[0]
+    return x1 + swiglu_ffn(h2[None], w["wg"], w["wu"], w["wd"],
+                           getattr(spec, "ffn_act", "swiglu"))[0]

@@ -67,6 +67,11 @@ class StackConfig:
     softcap: float = 0.0                # 0 = no logit softcap
     gated: bool = False                 # double-width wq: [q ; gate]
     rope_layout: str = "neox"           # "neox" (half split) or "norm" (adjacent pairs)
+    rope_rot_dim: int = 0               # rotated channels per head; 0 = head_dim
+    rope_mscale: float = 1.0            # attention factor on the rotated channels
+    rope_freq_factors: Optional[tuple] = None   # per-pair divisors of the frequency
+    ffn_act: str = "swiglu"             # "swiglu" or "geglu" (gated GELU)
+    window: int = 0                     # sliding window in keys; 0 = none
     seed: int = 0
 
     @property
@@ -111,6 +116,7 @@ class DecodeConfig:
     gated: bool
     weight_dtype: str = "bf16"
     rms_eps: float = 1e-5
+    ffn_act: str = "swiglu"             # "swiglu" or "geglu" (gated GELU)
     seed: int = 0
 
     @property
@@ -130,7 +136,7 @@ class DecodeConfig:
             head_dim=self.head_dim, d_ff=self.d_ff, batch=1,
             start_pos=self.rows, rope_theta=5e5,
             weight_dtype=self.weight_dtype, rms_eps=self.rms_eps,
-            softcap=self.softcap, gated=self.gated, seed=self.seed)
+            softcap=self.softcap, gated=self.gated, ffn_act=self.ffn_act, seed=self.seed)
 
     def replace(self, **kw) -> "DecodeConfig":
         return dataclasses.replace(self, **kw)

@@ -108,18 +108,21 @@ def test_layer_admission_predicates(ddl):
     assert ddl.ddl_layer_supported(ddl.layer_desc(**ok))
     assert ddl.ddl_layer_blob_bytes(ddl.layer_desc(**ok)) >= 2 * 100663296
     refusals = [
-        (dict(act=ddl.DDL_ACT_GELU), "SwiGLU"),
+        (dict(act=7), "activation"),
         (dict(post_norm_eps=1e-6), "epsilon"),
         (dict(v_head_dim=64), "v_head_dim"),
-        (dict(window=4096), "window"),
+        (dict(window=-1), "window"),
         (dict(has_post_attn_norm=1), "post"),
         (dict(has_post_ffn_norm=1), "post"),
         (dict(has_sinks=1), "sinks"),
         (dict(has_alibi=1), "ALiBi"),
         (dict(has_lora=1), "LoRA"),
-        (dict(rope_layout=ddl.DDL_ROPE_NORM), "layout"),
-        (dict(rope_rot_dim=64), "partial"),
-        (dict(rope_mscale=0.5), "factor"),
+        (dict(rope_layout=5), "layout"),
+        (dict(rope_rot_dim=96), "multiple of 64"),          # Neox pairs e, e+48
+        (dict(rope_rot_dim=130, rope_layout=ddl.DDL_ROPE_NORM), "head_dim"),
+        (dict(rope_rot_dim=63, rope_layout=ddl.DDL_ROPE_NORM), "even"),
+        (dict(rope_mscale=float("inf")), "factor"),
+        (dict(rope_freq_factors=[1.0] * 63 + [0.0]), "frequency factor"),
     ]
     for extra, why in refusals:
         d = ddl.layer_desc(**ok, **extra)
@@ -129,8 +132,14 @@ def test_layer_admission_predicates(ddl):
     assert not ddl.ddl_layer_supported(ddl.layer_desc(3072, 24, 8, 96, 8192))
     assert not ddl.ddl_layer_supported(ddl.layer_desc(3072, 24, 7, 128, 8192))
     assert not ddl.ddl_layer_supported(ddl.layer_desc(3000, 24, 8, 128, 8192))
-    # a layer without RoPE is served
+    # a layer without RoPE is served, and so are the RoPE, activation and
+    # window options the kernels implement
     assert ddl.ddl_layer_supported(ddl.layer_desc(**ok, rope_theta=None))
+    served = [dict(act=ddl.DDL_ACT_GELU), dict(window=4096), dict(rope_layout=ddl.DDL_ROPE_NORM),
+              dict(rope_layout=ddl.DDL_ROPE_NORM, rope_rot_dim=96), dict(rope_rot_dim=64),
+              dict(rope_mscale=0.5), dict(rope_freq_factors=[1.0 + i / 8 for i in range(64)])]
+    for extra in served:
+        assert ddl.ddl_layer_supported(ddl.layer_desc(**ok, **extra)), (extra, ddl.ddl_last_error())
 
 
 def test_blob_bytes_cover_the_packed_matrices(ddl):

@@ -114,7 +114,9 @@ def small_cfg(**kw):
                                 # other group sizes
                                 dict(n_heads=4, n_kv_heads=1, rows=700, softcap=10.0),
                                 dict(n_heads=8, n_kv_heads=8, rows=333, gated=True),
-                                dict(n_heads=16, n_kv_heads=16, head_dim=64, rows=65)])
+                                dict(n_heads=16, n_kv_heads=16, head_dim=64, rows=65),
+                                # the GELU-gated FFN in the decode tail
+                                dict(ffn_act="geglu", rows=257, gated=True, softcap=30.0)])
 def test_decode_shapes(ddl, kw):
     cfg = small_cfg(**kw)
     inp = synth.decode_inputs(cfg)
@@ -176,3 +178,22 @@ def test_capacity_rule(ddl):
     assert "capacity" in ddl.ddl_last_error()
     assert ddl.ddl_mirror_plan_capacity(512) == 1024
     assert ddl.ddl_mirror_plan_capacity(512, 2048) == 2048
+
+
+def test_windowed_layer_is_declined_untouched(ddl):
+    # a sliding-window layer is not served by the single-token path: declined
+    # before any device work, the mirror keeps its rows and seq_len
+    from dense_decoder_layer_amd.workloads import desc_for
+    cfg = small_cfg(rows=50)
+    inp = synth.decode_inputs(cfg)
+    dec = Decode(ddl, cfg, inp)
+    dec.layer = ddl.pack_layer_from_host(dec.ctx, desc_for(cfg.stack_view().replace(window=16)),
+                                         inp["weights"])
+    assert dec.upload(inp["cache_k"], inp["cache_v"], cfg.rows) == 1
+    dec.out.fill_(7.0)
+    rc = dec.step(cfg.rows, inp["q"], inp["k"], inp["v"], None, inp["residual"])
+    assert rc == 0 and "window" in ddl.ddl_last_error()
+    assert ddl.ddl_mirror_seq_len(dec.mirror) == cfg.rows
+    assert torch.all(dec.out == 7.0)
+    k, _ = dec.mirror_rows(cfg.rows)
+    np.testing.assert_array_equal(k, inp["cache_k"][: cfg.rows])

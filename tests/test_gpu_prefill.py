@@ -113,6 +113,29 @@ SMALL_CASES = {
     # is split over K, so the gate columns get their partial sums added
     "llama3b-gated-softcap-2layers-b256": synth.STACK_CONFIGS["llama3b_pp512"].replace(
         n_layers=2, batch=256, gated=True, softcap=30.0),
+    # RoPE variants: adjacent-pair layout; a partial Neox width; a partial
+    # adjacent-pair width with per-pair frequency factors and an attention factor
+    "rope-norm-prefix50": small("rope-norm-prefix50", rope_layout="norm", batch=90, start_pos=50),
+    "rope-neox-rot64": small("rope-neox-rot64", rope_rot_dim=64, batch=70, start_pos=33),
+    "rope-norm-rot96-freq-mscale": small(
+        "rope-norm-rot96-freq-mscale", rope_layout="norm", rope_rot_dim=96, rope_mscale=0.75,
+        rope_freq_factors=tuple(1.0 + 0.25 * i for i in range(48)), batch=64, start_pos=100),
+    "rope-hd64-norm-freq": small("rope-hd64-norm-freq", n_heads=8, n_kv_heads=4, head_dim=64,
+                                 rope_layout="norm", rope_freq_factors=tuple([2.0] * 32),
+                                 batch=40),
+    # the GELU-gated FFN (fp32 and bf16 weights)
+    "geglu-b100": small("geglu-b100", ffn_act="geglu", batch=100, start_pos=20),
+    "geglu-fp32-extras": small("geglu-fp32-extras", ffn_act="geglu", weight_dtype="fp32",
+                               qkv_bias=True, qk_norm=True, batch=48),
+    # sliding windows: shorter than one key tile, not tile-aligned over a
+    # prefix, with softcap and gate, and longer than every key (no effect)
+    "window7-b80": small("window7-b80", window=7, batch=80),
+    "window100-prefix300-gated": small("window100-prefix300-gated", window=100, batch=150,
+                                       start_pos=300, gated=True, softcap=20.0, n_layers=3),
+    "window33-group8-b333": small("window33-group8-b333", n_heads=16, n_kv_heads=2,
+                                  d_model=1024, d_ff=1536, window=33, batch=333, start_pos=64),
+    "window-longer-than-keys": small("window-longer-than-keys", window=4096, batch=60,
+                                     start_pos=10),
 }
 
 
@@ -203,7 +226,7 @@ def test_declines_touch_nothing_and_runs_stop_at_ineligible_layer(ddl):
                                     bufs["hidden_out"], bufs["k_rows"], bufs["v_rows"],
                                     bufs["workspace"][:100])
     # a layer the kernels do not serve is declined at pack time
-    assert ddl.ddl_layer_pack(ctx, ddl.layer_desc(256, 4, 2, 64, 704, window=128), {},
+    assert ddl.ddl_layer_pack(ctx, ddl.layer_desc(256, 4, 2, 64, 704, has_sinks=1), {},
                               ddl.DDL_DTYPE_F32, bufs["workspace"]) is None
 
 

@@ -20,7 +20,8 @@ MUTANTS = {
     "rope_position_off_by_one": ("positions = start_pos + np.arange(B)",
                                  "positions = start_pos + 1 + np.arange(B)"),
     "gqa_map_modulo": ("return h // (n_heads // n_kv_heads)", "return h % n_kv_heads"),
-    "causal_leaks_next_key": ("<= (start_pos + np.arange(B))", "<= (start_pos + 1 + np.arange(B))"),
+    "causal_leaks_next_key": ("visible = np.arange(T)[None, :] <= pos",
+                              "visible = np.arange(T)[None, :] <= pos + 1"),
     "softcap_before_scale": (
         "s = (q[:, h, :] @ k_all[:, g, :].T) * scale\n        if softcap:\n"
         "            s = softcap * np.tanh(s / softcap)",
@@ -41,6 +42,16 @@ MUTANTS = {
     "silu_as_sigmoid": ("return z / (1.0 + np.exp(-z))", "return 1 / (1.0 + np.exp(-z))"),
     "prefix_v_reads_k": ("v_all = np.concatenate([_f64(prefix_v)",
                          "v_all = np.concatenate([_f64(prefix_k)"),
+    "window_off_by_one": ("visible &= np.arange(T)[None, :] > pos - window",
+                          "visible &= np.arange(T)[None, :] >= pos - window"),
+    "mscale_on_every_channel": ("x[..., :rd] *= mscale", "x *= mscale"),
+    "freq_factor_multiplies": ("inv_freq = inv_freq / _f64(freq_factors)",
+                               "inv_freq = inv_freq * _f64(freq_factors)"),
+    "rope_options_dropped": ("freq_factors=getattr(spec, \"rope_freq_factors\", None),",
+                             "freq_factors=None,"),
+    "gelu_tanh_form": ("return 0.5 * z * (1.0 + erf(z / np.sqrt(2.0)))",
+                       "return 0.5 * z * (1.0 + np.tanh(0.7978845608 * (z + 0.044715 * z ** 3)))"),
+    "geglu_runs_silu": ("a = gelu(g) if act == \"geglu\" else silu(g)", "a = silu(g)"),
     "decode_skips_new_row": ("k_all = np.concatenate([_f64(cache_k)[:rows], _f64(k)[None]])",
                              "k_all = np.concatenate([_f64(cache_k)[:rows], "
                              "_f64(cache_k)[rows - 1:rows]])"),

@@ -56,17 +56,18 @@ def rel(a, b):
 # brute-force attention: per token, per head, per key scalar loops in fp64
 
 
-def brute_attention(q, k_all, v_all, start_pos, softcap=0.0, gate=None):
+def brute_attention(q, k_all, v_all, start_pos, softcap=0.0, gate=None, window=0):
     B, Hq, hd = q.shape
     Hkv = k_all.shape[1]
     per_group = Hq // Hkv
     out = np.zeros((B, Hq, hd))
     for b in range(B):
         last = start_pos + b
+        first = max(0, last - window + 1) if window else 0
         for h in range(Hq):
             g = h // per_group
             scores = []
-            for j in range(last + 1):
+            for j in range(first, last + 1):
                 s = 0.0
                 for c in range(hd):
                     s += float(q[b, h, c]) * float(k_all[j, g, c])
@@ -79,8 +80,8 @@ def brute_attention(q, k_all, v_all, start_pos, softcap=0.0, gate=None):
             z = sum(e)
             for c in range(hd):
                 acc = 0.0
-                for j in range(last + 1):
-                    acc += e[j] / z * float(v_all[j, g, c])
+                for i, j in enumerate(range(first, last + 1)):
+                    acc += e[i] / z * float(v_all[j, g, c])
                 if gate is not None:
                     acc *= 1.0 / (1.0 + math.exp(-float(gate[b, h, c])))
                 out[b, h, c] = acc
@@ -99,6 +100,32 @@ def test_attention_matches_brute_force(B, S, softcap, gated):
     got = oracle.causal_gqa_attention(q, k_all, v_all, S, softcap, gate)
     want = brute_attention(q, k_all, v_all, S, softcap, gate)
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("B,S,window", [(4, 0, 2), (3, 5, 3), (4, 6, 1), (2, 3, 9)])
+def test_windowed_attention_matches_brute_force(B, S, window):
+    Hq, Hkv, hd = 4, 2, 8
+    q = 2.0 * RNG.standard_normal((B, Hq, hd))
+    k_all = 2.0 * RNG.standard_normal((S + B, Hkv, hd))
+    v_all = RNG.standard_normal((S + B, Hkv, hd))
+    got = oracle.causal_gqa_attention(q, k_all, v_all, S, 1.0, None, window)
+    want = brute_attention(q, k_all, v_all, S, 1.0, None, window)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def test_window_special_cases():
+    B, S, Hq, Hkv, hd = 4, 3, 4, 2, 8
+    q = RNG.standard_normal((B, Hq, hd))
+    k_all = RNG.standard_normal((S + B, Hkv, hd))
+    v_all = RNG.standard_normal((S + B, Hkv, hd))
+    # a window as long as every key is no window at all
+    np.testing.assert_array_equal(oracle.causal_gqa_attention(q, k_all, v_all, S, 0.0, None, S + B),
+                                  oracle.causal_gqa_attention(q, k_all, v_all, S))
+    # a window of one key: each token returns its own value row exactly
+    o = oracle.causal_gqa_attention(q, k_all, v_all, S, 0.0, None, 1)
+    for b in range(B):
+        for h in range(Hq):
+            assert np.array_equal(o[b, h], v_all[S + b, h // 2])
 
 
 def test_attention_single_key_returns_its_value():
@@ -222,6 +249,19 @@ def test_swiglu_matches_torch():
                                [0.0, 1 / (1 + math.exp(-1)), -2 / (1 + math.exp(2))], rtol=1e-15)
 
 
+def test_gelu_matches_torch_and_normal_cdf():
+    z = np.array([0.0, 1.0, -1.0, 3.5, -6.0, 0.25])
+    want = F.gelu(torch.from_numpy(z), approximate="none").numpy()
+    np.testing.assert_allclose(oracle.gelu(z), want, rtol=1e-14, atol=1e-300)
+    # Phi(1) = 0.8413447460685429 (standard normal table)
+    assert abs(oracle.gelu(np.array([1.0]))[0] - 0.8413447460685429) < 1e-15
+    h = RNG.standard_normal((3, 12))
+    wg, wu, wd = (RNG.standard_normal(s) for s in [(20, 12), (20, 12), (12, 20)])
+    th = torch.from_numpy(h)
+    ref = (F.gelu(th @ torch.from_numpy(wg).T) * (th @ torch.from_numpy(wu).T)) @ torch.from_numpy(wd).T
+    np.testing.assert_allclose(oracle.swiglu_ffn(h, wg, wu, wd, "geglu"), ref.numpy(), rtol=1e-12)
+
+
 # ---------------------------------------------------------------------------
 # RoPE
 
@@ -281,6 +321,40 @@ def test_rope_options_freq_factors_partial_and_mscale():
     ms = oracle.apply_rope(x, pos, 1e4, rot_dim=4, mscale=0.5)
     np.testing.assert_allclose(ms[..., :4], 0.5 * part[..., :4], atol=1e-15)
     assert np.array_equal(ms[..., 4:], x[..., 4:])
+
+
+def test_rope_options_hand_example():
+    # rot_dim 2 of 4 channels, position 1, attention factor 0.5: only the first
+    # pair turns (by 1 rad) and is halved; Norm and Neox pair the same channels
+    x = np.array([[[1.0, 0.0, 5.0, 7.0]]])
+    want = [0.5 * math.cos(1), 0.5 * math.sin(1), 5.0, 7.0]
+    for lay in ("norm", "neox"):
+        np.testing.assert_allclose(oracle.apply_rope(x, [1], 1e4, lay, rot_dim=2, mscale=0.5)[0, 0],
+                                   want, atol=1e-16)
+    # frequency factors divide each pair's frequency: factor 2 on pair 0
+    e0 = np.array([[[1.0, 0.0, 0.0, 0.0]]])
+    np.testing.assert_allclose(oracle.apply_rope(e0, [1], 1e4, "neox", freq_factors=[2.0, 1.0])[0, 0],
+                               [math.cos(0.5), 0.0, math.sin(0.5), 0.0], atol=1e-16)
+
+
+@pytest.mark.parametrize("layout", ["norm", "neox"])
+def test_projection_applies_every_rope_option(layout):
+    # one-hot k rows reveal the angle, factor and pairing the projection step
+    # applies: hd 8, rotated width 4, factors (1, 4), attention factor 2, position 3
+    spec = Spec(n_heads=2, n_kv_heads=1, head_dim=8, d_model=8, rope_theta=1e4,
+                rope_layout=layout, rope_rot_dim=4, rope_freq_factors=(1.0, 4.0), rope_mscale=2.0)
+    w = rand_layer(spec)
+    w["wk"] = np.eye(8)
+    h = np.eye(8)                       # token c's k is e_c
+    _, _, k, _ = oracle.project_qkv(h, w, spec, np.full(8, 3))
+    k = k[:, 0, :]
+    a0, a1 = 3.0, 3.0 * 1e4 ** (-2.0 / 4) / 4.0     # pair 0 and pair 1 angles
+    p0, p1 = ((0, 1), (2, 3)) if layout == "norm" else ((0, 2), (1, 3))
+    for (c0, c1), a in ((p0, a0), (p1, a1)):
+        np.testing.assert_allclose(k[c0][[c0, c1]], [2 * math.cos(a), 2 * math.sin(a)], atol=1e-15)
+        np.testing.assert_allclose(k[c1][[c0, c1]], [-2 * math.sin(a), 2 * math.cos(a)], atol=1e-15)
+    for c in (4, 5, 6, 7):              # past the rotated width: untouched, unscaled
+        np.testing.assert_array_equal(k[c], np.eye(8)[c])
 
 
 # ---------------------------------------------------------------------------
@@ -357,7 +431,8 @@ def test_layer_residual_structure():
     h2 = F.rms_norm(x1, (spec1.d_model,), t(w["g_ffn"]), eps=spec1.rms_eps)
     want = x1 + (F.silu(h2 @ t(w["wg"]).T) * (h2 @ t(w["wu"]).T)) @ t(w["wd"]).T
     got, _, v_rows = oracle.dense_layer(x, w, spec1, 0)
-    np.testing.assert_allclose(got, want.numpy(), rtol=1e-12)
+    # absolute floor: fp64 rounding of O(1) sums, for entries that land near zero
+    np.testing.assert_allclose(got, want.numpy(), rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(v_rows, v.numpy(), rtol=1e-13)
 
 
