@@ -154,7 +154,7 @@ def ddl_layer_blob_bytes(desc: LayerDesc) -> int:
 
 
 _WEIGHT_KEYS = ("wq", "wk", "wv", "wo", "wg", "wu", "wd", "g_attn", "g_ffn", "bq", "bk", "bv",
-                "q_norm", "k_norm")
+                "q_norm", "k_norm", "g_post_attn", "g_post_ffn")
 
 
 def ddl_layer_pack(ctx: Ctx, desc: LayerDesc, weights: Dict[str, torch.Tensor], dtype: int,

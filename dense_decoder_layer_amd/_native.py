@@ -48,6 +48,7 @@ class LayerWeights(ctypes.Structure):
         ("g_attn", c_void_p), ("g_ffn", c_void_p),
         ("bq", c_void_p), ("bk", c_void_p), ("bv", c_void_p),
         ("q_norm", c_void_p), ("k_norm", c_void_p),
+        ("g_post_attn", c_void_p), ("g_post_ffn", c_void_p),
     ]
 
 

@@ -37,7 +37,6 @@ const char* why_unsupported(const ddl_layer_desc* d) {
     if (d->post_norm_eps != d->rms_eps) return "post-norm epsilon differs from rms_eps";
     if (d->v_head_dim != d->head_dim) return "v_head_dim differs from head_dim";
     if (d->window < 0) return "negative sliding window";
-    if (d->has_post_attn_norm || d->has_post_ffn_norm) return "post-attention/post-FFN norm";
     if (d->has_sinks) return "attention sinks";
     if (d->has_alibi) return "ALiBi";
     if (d->has_lora) return "LoRA adapter attached";
@@ -68,7 +67,7 @@ const char* why_unsupported(const ddl_layer_desc* d) {
 }
 
 struct BlobLayout {
-    size_t hdr, g_attn, g_ffn, bqkv, qn, kn, freq, wqkv, wo, wgu, wd, total;
+    size_t hdr, g_attn, g_ffn, bqkv, qn, kn, freq, gpa, gpf, wqkv, wo, wgu, wd, total;
     int nqkv;
 };
 
@@ -90,6 +89,8 @@ void blob_layout(const ddl_layer_desc* d, BlobLayout* L) {
     L->kn = take(d->has_qk_norm ? (size_t)d->head_dim * 4 : 0);
     const int rd = d->rope_rot_dim == 0 ? d->head_dim : d->rope_rot_dim;
     L->freq = take(d->rope_enabled && d->rope_freq_factors ? (size_t)(rd / 2) * 4 : 0);
+    L->gpa = take(d->has_post_attn_norm ? dm * 4 : 0);
+    L->gpf = take(d->has_post_ffn_norm ? dm * 4 : 0);
     L->wqkv = take((size_t)L->nqkv * dm * 2);
     L->wo = take(dm * qw * 2);
     L->wgu = take(2 * f * dm * 2);
@@ -142,11 +143,13 @@ WsLayout ws_layout(const ddl_layer* L, int B, int S) {
     return w;
 }
 
-// Layers of one run share the shapes the workspace is laid out for; per-layer
-// options (RoPE, activation, window, softcap, extras) may differ.
+// Layers of one run share the shapes the workspace is laid out for and the
+// model's one epsilon (a norm kernel may finish one layer and start the
+// next); per-layer options (RoPE, activation, window, softcap, extras,
+// sandwich norms) may differ.
 bool same_run_shape(const ddl_layer* a, const ddl_layer* b) {
     return a->d == b->d && a->hq == b->hq && a->hkv == b->hkv && a->hd == b->hd && a->f == b->f &&
-           a->gated == b->gated;
+           a->gated == b->gated && a->eps == b->eps;
 }
 
 // Two rotating layers whose position tables are the same.
@@ -255,6 +258,8 @@ int ddl_layer_pack(ddl_ctx* ctx, const ddl_layer_desc* d, const ddl_layer_weight
         return fail(DDL_ERR_INVALID, "q/k/v bias pointers are null");
     if (d->has_qk_norm && (!w->q_norm || !w->k_norm))
         return fail(DDL_ERR_INVALID, "q/k norm pointers are null");
+    if ((d->has_post_attn_norm && !w->g_post_attn) || (d->has_post_ffn_norm && !w->g_post_ffn))
+        return fail(DDL_ERR_INVALID, "post-norm gain pointers are null");
     BlobLayout B;
     blob_layout(d, &B);
     if (blob_bytes < B.total) return fail(DDL_ERR_INVALID, "blob smaller than ddl_layer_blob_bytes");
@@ -295,6 +300,8 @@ int ddl_layer_pack(ddl_ctx* ctx, const ddl_layer_desc* d, const ddl_layer_weight
     L->bqkv = d->has_qkv_bias ? reinterpret_cast<float*>(base + B.bqkv) : nullptr;
     L->q_norm = d->has_qk_norm ? reinterpret_cast<float*>(base + B.qn) : nullptr;
     L->k_norm = d->has_qk_norm ? reinterpret_cast<float*>(base + B.kn) : nullptr;
+    L->g_post_attn = d->has_post_attn_norm ? reinterpret_cast<float*>(base + B.gpa) : nullptr;
+    L->g_post_ffn = d->has_post_ffn_norm ? reinterpret_cast<float*>(base + B.gpf) : nullptr;
     L->wqkv = reinterpret_cast<f16*>(base + B.wqkv);
     L->wo = reinterpret_cast<f16*>(base + B.wo);
     L->wgu = reinterpret_cast<f16*>(base + B.wgu);
@@ -332,6 +339,10 @@ int ddl_layer_pack(ddl_ctx* ctx, const ddl_layer_desc* d, const ddl_layer_weight
         if (!e) e = hipMemcpyAsync(L->bqkv + qw, w->bk, kw * 4, hipMemcpyDefault, s);
         if (!e) e = hipMemcpyAsync(L->bqkv + qw + kw, w->bv, kw * 4, hipMemcpyDefault, s);
     }
+    if (!e && L->g_post_attn)
+        e = hipMemcpyAsync(L->g_post_attn, w->g_post_attn, dm * 4, hipMemcpyDefault, s);
+    if (!e && L->g_post_ffn)
+        e = hipMemcpyAsync(L->g_post_ffn, w->g_post_ffn, dm * 4, hipMemcpyDefault, s);
     if (!e && L->freq)   // from the handle's own copy: the caller's array may go away
         e = hipMemcpyAsync(L->freq, L->freq_host.data(), L->freq_host.size() * 4,
                            hipMemcpyHostToDevice, s);
@@ -418,6 +429,7 @@ int ddl_prefill_dense_stack(ddl_ctx* ctx, const float* hidden, const ddl_layer* 
     const int sp_wo = gemm_splits(batch, d, hq * hd, EPI_RESID);
     const int sp_down = gemm_splits(batch, d, f, EPI_RESID);
     int pending = 0;                  // partials of the last down projection
+    const float* pending_gpost = nullptr;   // its layer's post-FFN gain: hidden_out holds the raw branch
 
     hipError_t e = hipSuccess;
     const ddl_layer* table_of = nullptr;   // layer whose RoPE description the table holds
@@ -430,10 +442,14 @@ int ddl_prefill_dense_stack(ddl_ctx* ctx, const float* hidden, const ddl_layer* 
         }
         // the first layer reads the caller's hidden (no partials: never written)
         float* x = l == 0 ? const_cast<float*>(hidden) : hidden_out;
-        // attention branch: x1 = x + wo . attn(rope(qkv(rms_norm(x))))
+        // attention branch: x1 = x + wo . attn(rope(qkv(rms_norm(x)))); a
+        // sandwich-norm layer adds rms_norm(wo . attn) * g_post_attn instead.
+        // This norm also finishes the previous layer: its down partials, and
+        // with a post-FFN norm x = x1 + rms_norm(branch) * g_post_ffn.
         {
             ProbeScope p(ctx, DDL_K_RMSNORM, s);
-            e = launch_rmsnorm_f16(x, L->g_attn, h, batch, d, L->eps, part, pending, s);
+            e = launch_rmsnorm_f16(x, L->g_attn, h, batch, d, L->eps, part, pending,
+                                   pending_gpost ? x1 : nullptr, pending_gpost, s);
         }
         if (!e && start_pos > 0) {
             StagePrefixArgs sp{};
@@ -482,14 +498,15 @@ int ddl_prefill_dense_stack(ddl_ctx* ctx, const float* hidden, const ddl_layer* 
             g.A = o16; g.lda = hq * hd; g.W = L->wo; g.ldw = hq * hd;
             g.M = batch; g.N = d; g.K = hq * hd;
             g.inv_scale = &L->hdr->inv_scale[MAT_O];
-            g.C = x1; g.ldc = d; g.R = x; g.ldr = d; g.P = part;
+            g.C = x1; g.ldc = d; g.R = L->g_post_attn ? nullptr : x; g.ldr = d; g.P = part;
             ProbeScope p(ctx, DDL_K_GEMM_WO, s);
             e = launch_gemm(g, EPI_RESID, sp_wo, s);
         }
         // FFN branch: out = x1 + down(silu(gate(h2)) * up(h2)), h2 = rms_norm(x1)
         if (!e) {
             ProbeScope p(ctx, DDL_K_RMSNORM, s);
-            e = launch_rmsnorm_f16(x1, L->g_ffn, h, batch, d, L->eps, part, sp_wo - 1, s);
+            e = launch_rmsnorm_f16(x1, L->g_ffn, h, batch, d, L->eps, part, sp_wo - 1,
+                                   L->g_post_attn ? x : nullptr, L->g_post_attn, s);
         }
         if (!e) {
             GemmArgs g{};
@@ -505,12 +522,20 @@ int ddl_prefill_dense_stack(ddl_ctx* ctx, const float* hidden, const ddl_layer* 
             g.A = a16; g.lda = f; g.W = L->wd; g.ldw = f;
             g.M = batch; g.N = d; g.K = f;
             g.inv_scale = &L->hdr->inv_scale[MAT_D];
-            g.C = hidden_out; g.ldc = d; g.R = x1; g.ldr = d; g.P = part;
-            const int sp = l + 1 < run ? sp_down : 1;
+            g.C = hidden_out; g.ldc = d; g.R = L->g_post_ffn ? nullptr : x1; g.ldr = d; g.P = part;
+            // the run's last down projection splits only when a norm kernel
+            // follows it anyway (a post-FFN norm)
+            const int sp = l + 1 < run || L->g_post_ffn ? sp_down : 1;
             ProbeScope p(ctx, DDL_K_GEMM_DOWN, s);
             e = launch_gemm(g, EPI_RESID, sp, s);
             pending = sp - 1;
+            pending_gpost = L->g_post_ffn;
         }
+    }
+    if (!e && pending_gpost) {   // the last layer's post-FFN norm and residual
+        ProbeScope p(ctx, DDL_K_RMSNORM, s);
+        e = launch_rmsnorm_f16(hidden_out, nullptr, nullptr, batch, d, layers[run - 1]->eps, part,
+                               pending, x1, pending_gpost, s);
     }
     if (e) return fail(DDL_ERR_DEVICE, std::string("prefill launch: ") + hipGetErrorString(e));
     g_err.clear();
@@ -635,6 +660,9 @@ int ddl_attn_layer(ddl_ctx* ctx, ddl_mirror* m, int host_rows, const float* q, c
     // "frink-models 0.38.0 src/decoder/device_attention.rs",
     // device_attention_shape_ok: no sliding window on this path
     if (L->window != 0) return fail(DDL_DECLINED, "sliding-window layer");
+    // the decode tail's GEMVs add the residual in their epilogue: a layer
+    // with sandwich norms takes the host path
+    if (L->g_post_attn || L->g_post_ffn) return fail(DDL_DECLINED, "post-attention/post-FFN norm");
     if (!(softcap >= 0.0f)) return fail(DDL_ERR_INVALID, "negative softcap");
     const AttnWs W = attn_ws(L);
     if (!workspace || workspace_bytes < W.total)

@@ -7,7 +7,8 @@
 // Epilogues (the steps between the matmuls of a layer, fused into the
 // matmul that produces their input):
 //   EPI_F32     store fp32 (the stacked q/k/v/gate projection)
-//   EPI_RESID   C = R + acc (wo and down projections plus the residual)
+//   EPI_RESID   C = R + acc (wo and down projections plus the residual;
+//               with R null, C = acc for a layer whose branch is normed first)
 //   EPI_SWIGLU  W rows are gate/up interleaved in 16-row blocks; store
 //               fp16 silu(gate) * up into H[M][N/2]
 //   EPI_GEGLU   the same with the exact GELU, gate * Phi(gate), in place of
@@ -122,6 +123,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, floatx16 (&acc)[MI][
                     continue;
                 }
                 if constexpr (EPI == EPI_RESID) {
+                    if (p.R)   // null: the raw branch output (a sandwich norm follows)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);

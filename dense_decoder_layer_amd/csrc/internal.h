@@ -74,6 +74,7 @@ struct ddl_layer {
     size_t blob_bytes;
     BlobHeader* hdr;
     float *g_attn, *g_ffn, *bqkv, *q_norm, *k_norm;
+    float *g_post_attn, *g_post_ffn;   // sandwich-norm gains, or null
     f16 *wqkv, *wo, *wgu, *wd;
 };
 
@@ -93,7 +94,7 @@ struct GemmArgs {
     int M, N, K;
     const float* inv_scale;     // device scalar, multiplies the accumulator
     float* C; int ldc;          // EPI_F32, EPI_RESID output
-    const float* R; int ldr;    // EPI_RESID residual input (may alias C)
+    const float* R; int ldr;    // EPI_RESID residual input (may alias C; null: C = acc)
     f16* H; int ldh;            // EPI_SWIGLU / EPI_GEGLU output [M][N/2]
     // Split-K (EPI_F32, EPI_RESID): slice 0 of the K range applies the
     // epilogue to C; slice z > 0 stores its raw scaled sum to
@@ -107,12 +108,14 @@ bool gemm_shape_ok(int M, int N, int K, int epi);
 // The K split launch_gemm is to be called with for this shape (1 = none).
 int gemm_splits(int M, int N, int K, int epi);
 
-// h = rms_norm(x) * g as fp16, one row of d values per token.
-// h = fp16(rms_norm(x) * g).  With nparts > 0, x first gets the split-K
-// partials part[z * rows * d + row * d + col] (z < nparts) added and the sum
-// is written back to x.
+// h = fp16(rms_norm(x) * g), one row of d values per token.  With
+// nparts > 0, x first gets the split-K partials part[z * rows * d + row * d +
+// col] (z < nparts) added.  With gpost, that sum y becomes base + rms_norm(y)
+// * gpost (a sandwich norm's residual add).  x is written back when either
+// applies; h may be null (no second norm).
 hipError_t launch_rmsnorm_f16(float* x, const float* g, f16* h, int rows, int d, float eps,
-                              const float* part, int nparts, hipStream_t s);
+                              const float* part, int nparts, const float* base,
+                              const float* gpost, hipStream_t s);
 
 // tab[b][i] = m * (cos, sin) of (start_pos + b) * theta^(-2i/rot_dim) / freq[i]
 // for the rot_dim/2 rotated pairs i (freq may be null: factors of 1).

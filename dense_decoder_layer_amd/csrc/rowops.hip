@@ -18,57 +18,86 @@ namespace {
 // normalised and stored as fp16.
 constexpr int RMS_V4 = 4;   // float4s per thread: 256 * 4 * 4 = 4096 columns
 
-// With NP > 0 the split-K partials of the GEMM that produced x are added
-// first (in slice order) and the sum is written back to x.  The partial
-// count is a template parameter so every load of the row is issued before
-// the first add (one memory round trip, not one per slice).
-template <int NP>
+// With nparts > 0 the split-K partials of the GEMM that produced x are
+// added first (in slice order).  With gpost (a sandwich-norm layer's
+// post-attention or post-FFN gain, "frink-models 0.29.0
+// src/decoder/cuda_prefill.rs", cuda_prefill_layer: post_attn_norm,
+// post_ffn_norm) that sum is the branch output y and the row becomes
+// base + rms_norm(y) * gpost, the residual added after the branch's own norm.
+// The row is written back to x when it changed; h (null: skipped) gets
+// fp16(rms_norm(row) * g).
 __global__ __launch_bounds__(256) void rmsnorm_f16_kernel(float* __restrict__ x,
                                                           const float* __restrict__ g,
                                                           f16* __restrict__ h, int d, float eps,
                                                           const float* __restrict__ part,
-                                                          size_t pstride) {
+                                                          int nparts, size_t pstride,
+                                                          const float* __restrict__ base,
+                                                          const float* __restrict__ gpost) {
     __shared__ float red[4];
     const size_t row = blockIdx.x;
     float4* xr = reinterpret_cast<float4*>(x + row * d);
-    const float4* gr = reinterpret_cast<const float4*>(g);
     const int n4 = d >> 2;
     const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 v[RMS_V4], w[RMS_V4], q[NP > 0 ? NP : 1][RMS_V4];
+    float4 v[RMS_V4];
 #pragma unroll
     for (int k = 0; k < RMS_V4; ++k) {
         const int i = threadIdx.x + k * 256;
         v[k] = i < n4 ? xr[i] : zero;
-        w[k] = i < n4 ? gr[i] : zero;
-#pragma unroll
-        for (int z = 0; z < NP; ++z)
-            q[z][k] = i < n4 ? reinterpret_cast<const float4*>(part + z * pstride + row * d)[i] : zero;
     }
-    if constexpr (NP > 0) {
-#pragma unroll
-        for (int z = 0; z < NP; ++z)
+    if (nparts > 0) {
+        for (int z = 0; z < nparts; ++z) {
+            const float4* pr = reinterpret_cast<const float4*>(part + z * pstride + row * d);
 #pragma unroll
             for (int k = 0; k < RMS_V4; ++k) {
-                v[k].x += q[z][k].x; v[k].y += q[z][k].y; v[k].z += q[z][k].z; v[k].w += q[z][k].w;
+                const int i = threadIdx.x + k * 256;
+                if (i < n4) {
+                    const float4 q = pr[i];
+                    v[k].x += q.x; v[k].y += q.y; v[k].z += q.z; v[k].w += q.w;
+                }
             }
+        }
+    }
+    auto row_scale = [&]() {
+        float ss = 0.f;
+#pragma unroll
+        for (int k = 0; k < RMS_V4; ++k)
+            ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
+        ss = block_sum_256(ss, red);
+        return 1.0f / sqrtf(ss / (float)d + eps);
+    };
+    if (gpost) {
+        const float r = row_scale();
+        const float4* br = reinterpret_cast<const float4*>(base + row * d);
+        const float4* pg = reinterpret_cast<const float4*>(gpost);
+#pragma unroll
+        for (int k = 0; k < RMS_V4; ++k) {
+            const int i = threadIdx.x + k * 256;
+            if (i < n4) {
+                const float4 b = br[i], gp = pg[i];
+                v[k] = make_float4(b.x + v[k].x * r * gp.x, b.y + v[k].y * r * gp.y,
+                                   b.z + v[k].z * r * gp.z, b.w + v[k].w * r * gp.w);
+            }
+        }
+    }
+    if (nparts > 0 || gpost) {
 #pragma unroll
         for (int k = 0; k < RMS_V4; ++k) {
             const int i = threadIdx.x + k * 256;
             if (i < n4) xr[i] = v[k];
         }
     }
-    float ss = 0.f;
-#pragma unroll
-    for (int k = 0; k < RMS_V4; ++k) ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
-    ss = block_sum_256(ss, red);
-    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+    if (!h) return;
+    const float4* gr = reinterpret_cast<const float4*>(g);
+    const float r = row_scale();
     half4* hr = reinterpret_cast<half4*>(h + row * d);
 #pragma unroll
     for (int k = 0; k < RMS_V4; ++k) {
         const int i = threadIdx.x + k * 256;
-        if (i < n4)
-            hr[i] = half4{(f16)(v[k].x * r * w[k].x), (f16)(v[k].y * r * w[k].y),
-                          (f16)(v[k].z * r * w[k].z), (f16)(v[k].w * r * w[k].w)};
+        if (i < n4) {
+            const float4 w = gr[i];
+            hr[i] = half4{(f16)(v[k].x * r * w.x), (f16)(v[k].y * r * w.y),
+                          (f16)(v[k].z * r * w.z), (f16)(v[k].w * r * w.w)};
+        }
     }
 }
 
@@ -341,16 +370,12 @@ int grid_for(size_t n) {
 }  // namespace
 
 hipError_t launch_rmsnorm_f16(float* x, const float* g, f16* h, int rows, int d, float eps,
-                              const float* part, int nparts, hipStream_t s) {
-    if (d % 4 || d > 256 * 4 * RMS_V4 || nparts < 0 || nparts > 3 || (nparts > 0 && !part))
+                              const float* part, int nparts, const float* base,
+                              const float* gpost, hipStream_t s) {
+    if (d % 4 || d > 256 * 4 * RMS_V4 || (nparts > 0 && !part) || (gpost && !base) || (h && !g))
         return hipErrorInvalidValue;
-    const size_t ps = (size_t)rows * d;
-    switch (nparts) {
-        case 0: hipLaunchKernelGGL(rmsnorm_f16_kernel<0>, dim3(rows), dim3(256), 0, s, x, g, h, d, eps, part, ps); break;
-        case 1: hipLaunchKernelGGL(rmsnorm_f16_kernel<1>, dim3(rows), dim3(256), 0, s, x, g, h, d, eps, part, ps); break;
-        case 2: hipLaunchKernelGGL(rmsnorm_f16_kernel<2>, dim3(rows), dim3(256), 0, s, x, g, h, d, eps, part, ps); break;
-        case 3: hipLaunchKernelGGL(rmsnorm_f16_kernel<3>, dim3(rows), dim3(256), 0, s, x, g, h, d, eps, part, ps); break;
-    }
+    hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3(rows), dim3(256), 0, s, x, g, h, d, eps, part,
+                       nparts, (size_t)rows * d, base, gpost);
     return hipGetLastError();
 }
 

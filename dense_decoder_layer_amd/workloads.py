@@ -16,7 +16,8 @@ def desc_for(cfg):
     """ddl_layer_desc of a layer shaped like ``cfg`` (any object with the
     fields d_model, n_heads, n_kv_heads, head_dim, d_ff, rms_eps and,
     optionally, rope_theta, rope_layout, rope_rot_dim, rope_mscale,
-    rope_freq_factors, softcap, gated, qkv_bias, qk_norm, ffn_act, window)."""
+    rope_freq_factors, softcap, gated, qkv_bias, qk_norm, ffn_act, window,
+    post_norms)."""
     layout = {"neox": DDL_ROPE_NEOX, "norm": DDL_ROPE_NORM}[getattr(cfg, "rope_layout", "neox")]
     act = {"swiglu": DDL_ACT_SWIGLU, "geglu": DDL_ACT_GELU}[getattr(cfg, "ffn_act", "swiglu")]
     return layer_desc(cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.d_ff,
@@ -27,7 +28,9 @@ def desc_for(cfg):
                       rope_layout=layout, rope_rot_dim=getattr(cfg, "rope_rot_dim", 0),
                       rope_mscale=getattr(cfg, "rope_mscale", 1.0),
                       rope_freq_factors=getattr(cfg, "rope_freq_factors", None),
-                      act=act, window=getattr(cfg, "window", 0))
+                      act=act, window=getattr(cfg, "window", 0),
+                      has_post_attn_norm=int(getattr(cfg, "post_norms", False)),
+                      has_post_ffn_norm=int(getattr(cfg, "post_norms", False)))
 
 
 class DeviceStack:

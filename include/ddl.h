@@ -115,13 +115,15 @@ typedef struct {
  *   wg, wu [d_ff][d_model];  wd [d_model][d_ff]
  * fp32 vectors: g_attn, g_ffn [d_model]; bq [n_heads*head_dim], bk, bv
  * [n_kv_heads*head_dim] (when has_qkv_bias); q_norm, k_norm [head_dim]
- * (when has_qk_norm). */
+ * (when has_qk_norm); g_post_attn, g_post_ffn [d_model] (when
+ * has_post_attn_norm / has_post_ffn_norm: the sandwich norms' gains). */
 typedef struct {
     int dtype;
     const void *wq, *wk, *wv, *wo, *wg, *wu, *wd;
     const float *g_attn, *g_ffn;
     const float *bq, *bk, *bv;
     const float *q_norm, *k_norm;
+    const float *g_post_attn, *g_post_ffn;
 } ddl_layer_weights;
 
 /* 1 if the layer is one the kernels serve, 0 if not (pure host predicate;

@@ -48,6 +48,10 @@ pages leave open is a stated reading (the design doc lists them all):
   form) in place of silu.
 * A sliding window ``W`` lets the token at position ``p`` see keys
   ``p-W+1 .. p`` (its own key and the ``W-1`` before it).
+* A sandwich-norm layer RMS-normalises each branch output with its own gain
+  (``g_post_attn``, ``g_post_ffn``, the same epsilon) before the residual
+  add: ``x1 = x + rms_norm(attn) * g_post_attn``, ``out = x1 +
+  rms_norm(ffn) * g_post_ffn``.
 * The stack returns the last layer's residual stream, with no final norm.
 * The decode layer attends over the cached rows plus its own new row.
 
@@ -251,7 +255,9 @@ def dense_layer(x, w: Mapping[str, np.ndarray], spec, start_pos: int,
 
     fused_layer.rs (0.49.0), module doc: ``x + ffn(rms_norm(x + branch))``;
     cuda_prefill.rs (0.29.0), ``try_cuda_prefill_dense_stack``: each layer's
-    K/V rows come back, one ``kv_width`` row per token.
+    K/V rows come back, one ``kv_width`` row per token; ``cuda_prefill_
+    layer``: the optional post-attention and post-FFN norms (present when
+    ``w`` holds ``g_post_attn`` / ``g_post_ffn``).
     """
     x = _f64(x)
     B = x.shape[0]
@@ -267,9 +273,15 @@ def dense_layer(x, w: Mapping[str, np.ndarray], spec, start_pos: int,
     o = causal_gqa_attention(q, k_all, v_all, start_pos,
                              getattr(spec, "softcap", 0.0), gate,
                              getattr(spec, "window", 0))
-    x1 = x + o.reshape(B, -1) @ _f64(w["wo"]).T
+    attn = o.reshape(B, -1) @ _f64(w["wo"]).T
+    if "g_post_attn" in w:
+        attn = rms_norm(attn, w["g_post_attn"], spec.rms_eps)
+    x1 = x + attn
     h2 = rms_norm(x1, w["g_ffn"], spec.rms_eps)
-    x2 = x1 + swiglu_ffn(h2, w["wg"], w["wu"], w["wd"], getattr(spec, "ffn_act", "swiglu"))
+    ffn = swiglu_ffn(h2, w["wg"], w["wu"], w["wd"], getattr(spec, "ffn_act", "swiglu"))
+    if "g_post_ffn" in w:
+        ffn = rms_norm(ffn, w["g_post_ffn"], spec.rms_eps)
+    x2 = x1 + ffn
     return x2, k.reshape(B, Hkv * hd), v.reshape(B, Hkv * hd)
 
 

@@ -10,7 +10,7 @@ comes out the same.
 
 Distributions (the reading stated in the design doc):
   * projection matrices and biases  ~ N(0, 0.02)
-  * RMSNorm / QK-norm gains         ~ 1 + N(0, 0.02)
+  * RMSNorm / QK-norm / post-norm gains ~ 1 + N(0, 0.02)
   * hidden rows and prefix K/V rows ~ N(0, 1), fp32
   * decode-step q, k, v and gate    ~ N(0, 1), fp32
   * in a bf16 configuration the matrices are rounded to bf16 with
@@ -39,10 +39,10 @@ __all__ = [
 _SLOTS = {
     "g_attn": 0, "wq": 1, "wk": 2, "wv": 3, "bq": 4, "bk": 5, "bv": 6,
     "q_norm": 7, "k_norm": 8, "wo": 9, "g_ffn": 10, "wg": 11, "wu": 12,
-    "wd": 13, "prefix_k": 20, "prefix_v": 21,
+    "wd": 13, "g_post_attn": 14, "g_post_ffn": 15, "prefix_k": 20, "prefix_v": 21,
 }
 MATRICES = ("wq", "wk", "wv", "wo", "wg", "wu", "wd")
-VECTORS = ("g_attn", "bq", "bk", "bv", "q_norm", "k_norm", "g_ffn")
+VECTORS = ("g_attn", "bq", "bk", "bv", "q_norm", "k_norm", "g_ffn", "g_post_attn", "g_post_ffn")
 _HIDDEN_STREAM = 1
 _DECODE_STREAM_BASE = 1 << 20
 
@@ -72,6 +72,7 @@ class StackConfig:
     rope_freq_factors: Optional[tuple] = None   # per-pair divisors of the frequency
     ffn_act: str = "swiglu"             # "swiglu" or "geglu" (gated GELU)
     window: int = 0                     # sliding window in keys; 0 = none
+    post_norms: bool = False            # sandwich norms: post-attention and post-FFN gains
     seed: int = 0
 
     @property
@@ -96,6 +97,8 @@ class StackConfig:
             s.update(bq=(qw,), bk=(kw,), bv=(kw,))
         if self.qk_norm:
             s.update(q_norm=(self.head_dim,), k_norm=(self.head_dim,))
+        if self.post_norms:
+            s.update(g_post_attn=(d,), g_post_ffn=(d,))
         return s
 
     def replace(self, **kw) -> "StackConfig":
@@ -208,7 +211,7 @@ def _normal(seed: int, stream: int, shape, std: float = 1.0,
 
 def _layer_tensor(cfg: StackConfig, layer: int, name: str, shape) -> np.ndarray:
     stream = (layer + 1) * 32 + _SLOTS[name]
-    if name in ("g_attn", "g_ffn", "q_norm", "k_norm"):
+    if name in ("g_attn", "g_ffn", "q_norm", "k_norm", "g_post_attn", "g_post_ffn"):
         return _normal(cfg.seed, stream, shape, 0.02, 1.0)
     a = _normal(cfg.seed, stream, shape, 0.02)
     if name in MATRICES and cfg.weight_dtype == "bf16":

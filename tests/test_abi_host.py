@@ -112,8 +112,6 @@ def test_layer_admission_predicates(ddl):
         (dict(post_norm_eps=1e-6), "epsilon"),
         (dict(v_head_dim=64), "v_head_dim"),
         (dict(window=-1), "window"),
-        (dict(has_post_attn_norm=1), "post"),
-        (dict(has_post_ffn_norm=1), "post"),
         (dict(has_sinks=1), "sinks"),
         (dict(has_alibi=1), "ALiBi"),
         (dict(has_lora=1), "LoRA"),
@@ -137,7 +135,9 @@ def test_layer_admission_predicates(ddl):
     assert ddl.ddl_layer_supported(ddl.layer_desc(**ok, rope_theta=None))
     served = [dict(act=ddl.DDL_ACT_GELU), dict(window=4096), dict(rope_layout=ddl.DDL_ROPE_NORM),
               dict(rope_layout=ddl.DDL_ROPE_NORM, rope_rot_dim=96), dict(rope_rot_dim=64),
-              dict(rope_mscale=0.5), dict(rope_freq_factors=[1.0 + i / 8 for i in range(64)])]
+              dict(rope_mscale=0.5), dict(rope_freq_factors=[1.0 + i / 8 for i in range(64)]),
+              dict(has_post_attn_norm=1), dict(has_post_ffn_norm=1),
+              dict(has_post_attn_norm=1, has_post_ffn_norm=1)]
     for extra in served:
         assert ddl.ddl_layer_supported(ddl.layer_desc(**ok, **extra)), (extra, ddl.ddl_last_error())
 

@@ -197,3 +197,20 @@ def test_windowed_layer_is_declined_untouched(ddl):
     assert torch.all(dec.out == 7.0)
     k, _ = dec.mirror_rows(cfg.rows)
     np.testing.assert_array_equal(k, inp["cache_k"][: cfg.rows])
+
+
+def test_sandwich_norm_layer_is_declined_untouched(ddl):
+    from dense_decoder_layer_amd.workloads import desc_for
+    cfg = small_cfg(rows=20)
+    inp = synth.decode_inputs(cfg)
+    dec = Decode(ddl, cfg, inp)
+    w = dict(inp["weights"])
+    w["g_post_attn"] = np.ones(cfg.d_model, np.float32)
+    w["g_post_ffn"] = np.ones(cfg.d_model, np.float32)
+    dec.layer = ddl.pack_layer_from_host(dec.ctx, desc_for(cfg.stack_view().replace(post_norms=True)),
+                                         w)
+    assert dec.upload(inp["cache_k"], inp["cache_v"], cfg.rows) == 1
+    dec.out.fill_(7.0)
+    assert dec.step(cfg.rows, inp["q"], inp["k"], inp["v"], None, inp["residual"]) == 0
+    assert "post" in ddl.ddl_last_error()
+    assert ddl.ddl_mirror_seq_len(dec.mirror) == cfg.rows and torch.all(dec.out == 7.0)

@@ -136,6 +136,16 @@ SMALL_CASES = {
                                   d_model=1024, d_ff=1536, window=33, batch=333, start_pos=64),
     "window-longer-than-keys": small("window-longer-than-keys", window=4096, batch=60,
                                      start_pos=10),
+    # sandwich norms (post-attention and post-FFN): alone over a prefix, with
+    # the GELU FFN, window, softcap and gate, and at the 3B width where the
+    # wo/down projections split over K and the run's last down projection
+    # is finished by the closing norm
+    "post-norms-prefix40": small("post-norms-prefix40", post_norms=True, batch=72, start_pos=40),
+    "post-norms-geglu-window-softcap": small("post-norms-geglu-window-softcap", post_norms=True,
+                                             ffn_act="geglu", window=48, softcap=30.0, gated=True,
+                                             batch=130, n_layers=3),
+    "post-norms-llama3b-2layers-b256": synth.STACK_CONFIGS["llama3b_pp512"].replace(
+        n_layers=2, batch=256, post_norms=True),
 }
 
 

@@ -34,9 +34,9 @@ MUTANTS = {
     "qk_norm_dropped": ("        q = rms_norm(q, w[\"q_norm\"], spec.rms_eps)\n"
                         "        k = rms_norm(k, w[\"k_norm\"], spec.rms_eps)\n",
                         "        pass\n"),
-    "attn_residual_dropped": ("x1 = x + o.reshape(B, -1)", "x1 = 0 * x + o.reshape(B, -1)"),
-    "wo_transposed": ("x1 = x + o.reshape(B, -1) @ _f64(w[\"wo\"]).T",
-                      "x1 = x + o.reshape(B, -1) @ _f64(w[\"wo\"]).reshape("
+    "attn_residual_dropped": ("    x1 = x + attn\n", "    x1 = 0 * x + attn\n"),
+    "wo_transposed": ("attn = o.reshape(B, -1) @ _f64(w[\"wo\"]).T",
+                      "attn = o.reshape(B, -1) @ _f64(w[\"wo\"]).reshape("
                       "_f64(w[\"wo\"]).shape[::-1])"),
     "ffn_norm_reads_x": ("h2 = rms_norm(x1, w[\"g_ffn\"]", "h2 = rms_norm(x, w[\"g_ffn\"]"),
     "silu_as_sigmoid": ("return z / (1.0 + np.exp(-z))", "return 1 / (1.0 + np.exp(-z))"),
@@ -52,6 +52,11 @@ MUTANTS = {
     "gelu_tanh_form": ("return 0.5 * z * (1.0 + erf(z / np.sqrt(2.0)))",
                        "return 0.5 * z * (1.0 + np.tanh(0.7978845608 * (z + 0.044715 * z ** 3)))"),
     "geglu_runs_silu": ("a = gelu(g) if act == \"geglu\" else silu(g)", "a = silu(g)"),
+    "post_attn_norm_after_residual": ("    x1 = x + attn\n",
+                                      "    x1 = x + attn\n    if \"g_post_attn\" in w:\n"
+                                      "        x1 = rms_norm(x + o.reshape(B, -1) @ _f64(w[\"wo\"]).T, "
+                                      "w[\"g_post_attn\"], spec.rms_eps)\n"),
+    "post_ffn_norm_dropped": ("        ffn = rms_norm(ffn, w[\"g_post_ffn\"], spec.rms_eps)", "        pass"),
     "decode_skips_new_row": ("k_all = np.concatenate([_f64(cache_k)[:rows], _f64(k)[None]])",
                              "k_all = np.concatenate([_f64(cache_k)[:rows], "
                              "_f64(cache_k)[rows - 1:rows]])"),

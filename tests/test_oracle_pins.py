@@ -436,6 +436,33 @@ def test_layer_residual_structure():
     np.testing.assert_allclose(v_rows, v.numpy(), rtol=1e-13)
 
 
+def test_sandwich_norms_closed_form_and_scale_invariance():
+    # one token, no prefix: attention returns v, so a sandwich-norm layer has
+    # a closed form in library calls
+    spec = Spec(rope_theta=None)
+    w = rand_layer(spec)
+    w.update(g_post_attn=1 + 0.1 * RNG.standard_normal(spec.d_model),
+             g_post_ffn=1 + 0.1 * RNG.standard_normal(spec.d_model))
+    x = RNG.standard_normal((1, spec.d_model))
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    n = lambda a, g: F.rms_norm(a, (spec.d_model,), t(g), eps=spec.rms_eps)
+    h = n(t(x), w["g_attn"])
+    v = h @ t(w["wv"]).T
+    o = v.reshape(1, spec.n_kv_heads, spec.head_dim).repeat_interleave(2, dim=1).reshape(1, -1)
+    x1 = t(x) + n(o @ t(w["wo"]).T, w["g_post_attn"])
+    h2 = n(x1, w["g_ffn"])
+    want = x1 + n((F.silu(h2 @ t(w["wg"]).T) * (h2 @ t(w["wu"]).T)) @ t(w["wd"]).T, w["g_post_ffn"])
+    got, _, _ = oracle.dense_layer(x, w, spec, 0)
+    np.testing.assert_allclose(got, want.numpy(), rtol=1e-12, atol=1e-13)
+    # with eps 0 each branch's scale is normalised away: scaling wo and wd
+    # leaves a 3-token output unchanged
+    spec0 = Spec(rms_eps=0.0)
+    x3 = RNG.standard_normal((3, spec.d_model))
+    a, _, _ = oracle.dense_layer(x3, w, spec0, 0)
+    b, _, _ = oracle.dense_layer(x3, dict(w, wo=7.0 * w["wo"], wd=0.01 * w["wd"]), spec0, 0)
+    np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-12)
+
+
 def test_returned_rows_are_rotated_k_and_v():
     spec = Spec(qk_norm=True, qkv_bias=True)
     w = rand_layer(spec)
