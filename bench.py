@@ -102,7 +102,7 @@ def decode_bench(ddl, ctx, reps=40):
     cfg = synth.DECODE_CONFIG
     inp = synth.decode_inputs(cfg)
     layer = ddl.pack_layer_from_host(ctx, desc_for(cfg.stack_view()), inp["weights"])
-    cap = ddl.ddl_mirror_plan_capacity(cfg.rows, cfg.rows + 6 * reps + 16)   # every call appends a row
+    cap = ddl.ddl_mirror_plan_capacity(cfg.rows, cfg.rows + 9 * reps + 16)   # every call appends a row
     mirrors, bufs = [], []
     k = torch.from_numpy(inp["cache_k"]).cuda()
     v = torch.from_numpy(inp["cache_v"]).cuda()
@@ -154,11 +154,42 @@ def decode_bench(ddl, ctx, reps=40):
         d = ddl.ddl_probe_read(ctx, reps)
         ddl.ddl_probe_enable(ctx, kind, 0)
         tail[name + "_us"] = round(sum(d) / len(d) * 1e3, 2)
+    # the whole layer with its head on the device (ddl_decode_layer): RMS norm,
+    # stacked q/k/v/gate GEMV, bias/QK-norm/RoPE, then the same attention and tail
+    hid = t(inp["residual"])
+    k_row = torch.empty(cfg.kv_width, dtype=torch.float32, device="cuda")
+    v_row = torch.empty_like(k_row)
+
+    def dcall(i):
+        m = mirrors[i % 2]
+        rc = ddl.ddl_decode_layer(ctx, m, ddl.ddl_mirror_seq_len(m), hid, layer, out, k_row, v_row,
+                                  ws)
+        assert rc == 1, ddl.ddl_last_error()
+
+    for i in range(4):
+        dcall(i)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(reps):
+        dcall(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    full_ms = start.elapsed_time(end) / reps
+    for name, kind in (("gemv_qkv", ddl.DDL_K_GEMV_QKV), ("head", ddl.DDL_K_DECODE_HEAD)):
+        ddl.ddl_probe_enable(ctx, kind, reps)
+        for i in range(reps):
+            dcall(i)
+        torch.cuda.synchronize()
+        d = ddl.ddl_probe_read(ctx, reps)
+        ddl.ddl_probe_enable(ctx, kind, 0)
+        tail[name + "_us"] = round(sum(d) / len(d) * 1e3, 2)
     attn_bytes = attended * cfg.kv_width * 4 * 2 // reps     # fp32 K and V rows read per call
     return {"config": f"{cfg.name}: {cfg.rows} cached rows, {cfg.n_heads} q / {cfg.n_kv_heads} "
                       f"KV heads x {cfg.head_dim}, softcap {cfg.softcap:g}, sigmoid gate, "
                       f"wo + RMSNorm + SwiGLU {cfg.d_ff} tail, hidden {cfg.d_model}",
-            "ms_per_layer": round(layer_ms, 4), "attn_us": round(attn_ms * 1e3, 2),
+            "ms_per_layer": round(layer_ms, 4),
+            "decode_layer_ms": round(full_ms, 4),   # ddl_decode_layer: head on the device too
+            "attn_us": round(attn_ms * 1e3, 2),
             "attn_bytes": attn_bytes,
             "attn_hbm_gbs": round(attn_bytes / (attn_ms / 1e3) / 1e9, 1),
             "attn_hbm_frac": round(attn_bytes / (attn_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),

@@ -19,9 +19,10 @@ import numpy as np
 import torch
 
 from . import _native as N
-from ._native import (DDL_K_ATTN_PREFILL, DDL_K_DECODE_ATTN, DDL_K_GEMM_DOWN, DDL_K_GEMM_GATE_UP,
-                      DDL_K_GEMM_QKV, DDL_K_GEMM_WO, DDL_K_GEMV_DOWN, DDL_K_GEMV_GATE_UP,
-                      DDL_K_GEMV_WO, DDL_K_QKV_POST, DDL_K_RMSNORM)
+from ._native import (DDL_K_ATTN_PREFILL, DDL_K_DECODE_ATTN, DDL_K_DECODE_HEAD, DDL_K_GEMM_DOWN,
+                      DDL_K_GEMM_GATE_UP, DDL_K_GEMM_QKV, DDL_K_GEMM_WO, DDL_K_GEMV_DOWN,
+                      DDL_K_GEMV_GATE_UP, DDL_K_GEMV_QKV, DDL_K_GEMV_WO, DDL_K_QKV_POST,
+                      DDL_K_RMSNORM)
 from ._native import (DDL_ACT_GELU, DDL_ACT_SWIGLU, DDL_DECLINED, DDL_DTYPE_BF16,
                       DDL_DTYPE_F32, DDL_ERR_DEVICE, DDL_ERR_INJECTED, DDL_ERR_INVALID,
                       DDL_ERR_WORKSPACE, DDL_ROPE_NEOX, DDL_ROPE_NORM, CtxOpts, LayerDesc,
@@ -32,7 +33,8 @@ __all__ = [
     "ddl_layer_pack", "ddl_layer_destroy", "ddl_workspace_bytes", "ddl_prefill_dense_stack",
     "ddl_mirror_bytes", "ddl_mirror_init", "ddl_mirror_upload", "ddl_mirror_seq_len",
     "ddl_mirror_capacity", "ddl_mirror_invalidate", "ddl_mirror_plan_capacity",
-    "ddl_mirror_destroy", "ddl_attn_workspace_bytes", "ddl_attn_layer", "ddl_last_error",
+    "ddl_mirror_destroy", "ddl_attn_workspace_bytes", "ddl_attn_layer", "ddl_decode_layer",
+    "ddl_last_error",
     "ddl_probe_enable", "ddl_probe_read",
     "layer_desc", "pack_layer_from_host", "Ctx", "Layer", "Mirror", "LayerDesc",
 ]
@@ -295,4 +297,17 @@ def ddl_attn_layer(ctx: Ctx, mirror: Mirror, host_rows: int, q: torch.Tensor, k:
                                workspace.numel() * workspace.element_size(), _stream(stream))
     if rc < 0:
         raise RuntimeError(f"ddl_attn_layer: {rc} {ddl_last_error()}")
+    return rc
+
+
+def ddl_decode_layer(ctx: Ctx, mirror: Mirror, host_rows: int, hidden: torch.Tensor, layer: Layer,
+                     out: torch.Tensor, k_row: torch.Tensor, v_row: torch.Tensor,
+                     workspace: torch.Tensor, stream=None) -> int:
+    """Returns 1 (served), 0 (declined); raises on errors (< 0)."""
+    rc = _lib().ddl_decode_layer(ctx.handle, mirror.handle, host_rows, hidden.data_ptr(),
+                                 layer.handle, out.data_ptr(), k_row.data_ptr(), v_row.data_ptr(),
+                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                 _stream(stream))
+    if rc < 0:
+        raise RuntimeError(f"ddl_decode_layer: {rc} {ddl_last_error()}")
     return rc

@@ -17,7 +17,7 @@ DDL_ROPE_NEOX, DDL_ROPE_NORM = 0, 1
 DDL_DTYPE_F32, DDL_DTYPE_BF16 = 0, 1
 (DDL_K_RMSNORM, DDL_K_GEMM_QKV, DDL_K_QKV_POST, DDL_K_ATTN_PREFILL, DDL_K_GEMM_WO,
  DDL_K_GEMM_GATE_UP, DDL_K_GEMM_DOWN, DDL_K_DECODE_ATTN, DDL_K_GEMV_WO, DDL_K_GEMV_GATE_UP,
- DDL_K_GEMV_DOWN) = range(11)
+ DDL_K_GEMV_DOWN, DDL_K_GEMV_QKV, DDL_K_DECODE_HEAD) = range(13)
 
 
 class CtxOpts(ctypes.Structure):
@@ -78,6 +78,9 @@ SIGNATURES = {
     "ddl_attn_layer": (c_int, [
         c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_float,
         c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "ddl_decode_layer": (c_int, [
+        c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+        c_size_t, c_void_p]),
     "ddl_probe_enable": (c_int, [c_void_p, c_int, c_int]),
     "ddl_probe_read": (c_int, [c_void_p, POINTER(c_float), c_int]),
     "ddl_last_error": (c_char_p, []),

@@ -609,7 +609,7 @@ int ddl_mirror_plan_capacity(int rows, int planned) {
 
 namespace {
 struct AttnWs {
-    size_t pm, pl, po, o, x1, a, total;
+    size_t pm, pl, po, o, x1, a, qkv, q, total;
 };
 // Partials are sized for the largest split count, so one workspace serves
 // every row count.
@@ -628,56 +628,48 @@ AttnWs attn_ws(const ddl_layer* L) {
     w.o = take((size_t)L->hq * L->hd * 4);
     w.x1 = take((size_t)L->d * 4);
     w.a = take((size_t)L->f * 4);
+    w.qkv = take((size_t)L->nqkv * 4);      // ddl_decode_layer's head
+    w.q = take((size_t)L->hq * L->hd * 4);
     w.total = o;
     return w;
 }
-}  // namespace
 
-size_t ddl_attn_workspace_bytes(const ddl_layer* layer, int capacity) {
-    if (!layer || capacity <= 0) return 0;
-    return attn_ws(layer).total;
-}
-
-int ddl_attn_layer(ddl_ctx* ctx, ddl_mirror* m, int host_rows, const float* q, const float* k,
-                   const float* v, const float* gate, int n_heads, float softcap,
-                   const ddl_layer* L, const float* residual, float* out, void* workspace,
-                   size_t workspace_bytes, void* stream) {
-    if (!ctx || !m || !q || !k || !v || !L || !residual || !out)
-        return fail(DDL_ERR_INVALID, "null argument");
-    // refusals, before any device work ("frink-models 0.38.0
-    // src/decoder/device_attention.rs": the mirror is trusted only while it
-    // holds exactly the cache's rows, and needs room for one more)
+// The refusals of the single-token path, before any device work
+// ("frink-models 0.38.0 src/decoder/device_attention.rs": the mirror is
+// trusted only while it holds exactly the cache's rows and needs room for
+// one more; device_attention_shape_ok: no sliding window).  True when the
+// call is declined (the reason is in the last error).
+bool decode_refused(const ddl_mirror* m, int host_rows, int n_heads, const ddl_layer* L) {
+    auto no = [](const char* why) {
+        fail(DDL_DECLINED, why);
+        return true;
+    };
     if (m->seq_len != host_rows)
-        return fail(DDL_DECLINED, "mirror is stale (seq_len differs from the cache's rows)");
+        return no("mirror is stale (seq_len differs from the cache's rows)");
     if (host_rows < 0 || m->cap < host_rows + 1)
-        return fail(DDL_DECLINED, "mirror capacity below rows + 1");
+        return no("mirror capacity below rows + 1");
     if (n_heads != L->hq || m->hkv != L->hkv || m->hd != L->hd)
-        return fail(DDL_DECLINED, "head shape differs between call, layer and mirror");
+        return no("head shape differs between call, layer and mirror");
     if (!decode_group_ok(L->hq, L->hkv, L->hd))
-        return fail(DDL_DECLINED, "query-head group size not served");
+        return no("query-head group size not served");
     if (!gemv_shape_ok(L->d) || !gemv_shape_ok(L->f) || !gemv_shape_ok(L->hq * L->hd))
-        return fail(DDL_DECLINED, "GEMV width not served");
-    // "frink-models 0.38.0 src/decoder/device_attention.rs",
-    // device_attention_shape_ok: no sliding window on this path
-    if (L->window != 0) return fail(DDL_DECLINED, "sliding-window layer");
+        return no("GEMV width not served");
+    if (L->window != 0) return no("sliding-window layer");
     // the decode tail's GEMVs add the residual in their epilogue: a layer
     // with sandwich norms takes the host path
-    if (L->g_post_attn || L->g_post_ffn) return fail(DDL_DECLINED, "post-attention/post-FFN norm");
-    if (!(softcap >= 0.0f)) return fail(DDL_ERR_INVALID, "negative softcap");
-    const AttnWs W = attn_ws(L);
-    if (!workspace || workspace_bytes < W.total)
-        return fail(DDL_ERR_WORKSPACE, "workspace smaller than ddl_attn_workspace_bytes");
-    if (ctx->fault_after_admission) {
-        m->seq_len = -1;
-        return fail(DDL_ERR_INJECTED, "injected fault after admission");
-    }
+    if (L->g_post_attn || L->g_post_ffn) return no("post-attention/post-FFN norm");
+    return false;
+}
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    char* ws = static_cast<char*>(workspace);
+// Attention against the mirror (appending row host_rows) and the tail:
+// x1 = x + wo . o; out = x1 + down(act(gate(h2)) * up(h2)), h2 = rms_norm(x1).
+hipError_t attn_and_tail(ddl_ctx* ctx, ddl_mirror* m, int host_rows, const float* q,
+                         const float* k, const float* v, const float* gate, float softcap,
+                         const ddl_layer* L, const float* residual, float* out, char* ws,
+                         const AttnWs& W, hipStream_t s) {
     float* o = reinterpret_cast<float*>(ws + W.o);
     float* x1 = reinterpret_cast<float*>(ws + W.x1);
     float* a = reinterpret_cast<float*>(ws + W.a);
-
     DecodeAttnArgs d{};
     d.q = q; d.knew = k; d.vnew = v; d.mk = m->k; d.mv = m->v; d.gate = gate;
     d.part_m = reinterpret_cast<float*>(ws + W.pm);
@@ -700,7 +692,7 @@ int ddl_attn_layer(ddl_ctx* ctx, ddl_mirror* m, int host_rows, const float* q, c
         ProbeScope p(ctx, DDL_K_GEMV_WO, s);
         e = launch_gemv(g, GV_RESID, s);
     }
-    if (!e) {   // a = silu(gate(h2)) * up(h2), h2 = rms_norm(x1) * g_ffn
+    if (!e) {   // a = act(gate(h2)) * up(h2), h2 = rms_norm(x1) * g_ffn
         GemvArgs g{};
         g.W = L->wgu; g.K = L->d; g.N = L->f;
         g.inv_scale = &L->hdr->inv_scale[MAT_GU];
@@ -717,9 +709,87 @@ int ddl_attn_layer(ddl_ctx* ctx, ddl_mirror* m, int host_rows, const float* q, c
         ProbeScope p(ctx, DDL_K_GEMV_DOWN, s);
         e = launch_gemv(g, GV_RESID, s);
     }
+    return e;
+}
+}  // namespace
+
+size_t ddl_attn_workspace_bytes(const ddl_layer* layer, int capacity) {
+    if (!layer || capacity <= 0) return 0;
+    return attn_ws(layer).total;
+}
+
+int ddl_attn_layer(ddl_ctx* ctx, ddl_mirror* m, int host_rows, const float* q, const float* k,
+                   const float* v, const float* gate, int n_heads, float softcap,
+                   const ddl_layer* L, const float* residual, float* out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    if (!ctx || !m || !q || !k || !v || !L || !residual || !out)
+        return fail(DDL_ERR_INVALID, "null argument");
+    if (decode_refused(m, host_rows, n_heads, L)) return DDL_DECLINED;
+    if (!(softcap >= 0.0f)) return fail(DDL_ERR_INVALID, "negative softcap");
+    const AttnWs W = attn_ws(L);
+    if (!workspace || workspace_bytes < W.total)
+        return fail(DDL_ERR_WORKSPACE, "workspace smaller than ddl_attn_workspace_bytes");
+    if (ctx->fault_after_admission) {
+        m->seq_len = -1;
+        return fail(DDL_ERR_INJECTED, "injected fault after admission");
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = attn_and_tail(ctx, m, host_rows, q, k, v, gate, softcap, L, residual, out,
+                                       static_cast<char*>(workspace), W, s);
     if (e) {
         m->seq_len = -1;
         return fail(DDL_ERR_DEVICE, std::string("attn_layer launch: ") + hipGetErrorString(e));
+    }
+    m->seq_len = host_rows + 1;
+    g_err.clear();
+    return 1;
+}
+
+int ddl_decode_layer(ddl_ctx* ctx, ddl_mirror* m, int host_rows, const float* hidden,
+                     const ddl_layer* L, float* out, float* k_row, float* v_row,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    if (!ctx || !m || !hidden || !L || !out || !k_row || !v_row)
+        return fail(DDL_ERR_INVALID, "null argument");
+    if (decode_refused(m, host_rows, L->hq, L)) return DDL_DECLINED;
+    if (!gemv_shape_ok(L->d) || L->nqkv % 32) return fail(DDL_DECLINED, "GEMV width not served");
+    const AttnWs W = attn_ws(L);
+    if (!workspace || workspace_bytes < W.total)
+        return fail(DDL_ERR_WORKSPACE, "workspace smaller than ddl_attn_workspace_bytes");
+    if (ctx->fault_after_admission) {
+        m->seq_len = -1;
+        return fail(DDL_ERR_INJECTED, "injected fault after admission");
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    float* qkv = reinterpret_cast<float*>(ws + W.qkv);
+    float* q = reinterpret_cast<float*>(ws + W.q);
+    hipError_t e;
+    {   // qkv = [Wq; Wk; Wv(; Wgate)] . (rms_norm(x) * g_attn)
+        GemvArgs g{};
+        g.W = L->wqkv; g.K = L->d; g.N = L->nqkv;
+        g.inv_scale = &L->hdr->inv_scale[MAT_QKV];
+        g.x = hidden; g.norm_g = L->g_attn; g.eps = L->eps; g.r = nullptr; g.y = qkv;
+        ProbeScope p(ctx, DDL_K_GEMV_QKV, s);
+        e = launch_gemv(g, GV_RESID, s);
+    }
+    if (!e) {
+        DecodeHeadArgs h{};
+        h.qkv = qkv; h.bias = L->bqkv; h.q_norm = L->q_norm; h.k_norm = L->k_norm; h.eps = L->eps;
+        h.rope_on = L->rope_on; h.rope_layout = L->rope_layout; h.rot_dim = L->rot_dim;
+        h.theta = L->theta; h.freq = L->freq; h.mscale = L->mscale;
+        h.pos = host_rows; h.hq = L->hq; h.hkv = L->hkv; h.hd = L->hd;
+        h.q = q; h.k_row = k_row; h.v_row = v_row;
+        ProbeScope p(ctx, DDL_K_DECODE_HEAD, s);
+        e = launch_decode_head(h, s);
+    }
+    if (!e) {
+        const float* gate = L->gated ? qkv + (size_t)(L->hq + 2 * L->hkv) * L->hd : nullptr;
+        e = attn_and_tail(ctx, m, host_rows, q, k_row, v_row, gate, L->softcap, L, hidden, out, ws,
+                          W, s);
+    }
+    if (e) {
+        m->seq_len = -1;
+        return fail(DDL_ERR_DEVICE, std::string("decode_layer launch: ") + hipGetErrorString(e));
     }
     m->seq_len = host_rows + 1;
     g_err.clear();

@@ -474,7 +474,7 @@ __global__ __launch_bounds__(GV_WAVES * 64) void gemv_kernel(GemvArgs p) {
         if (tid < 16) p.y[nb * 16 + tid] = act * other;
     } else {
         const int row = nb * 32 + hsel * 16 + tid;
-        p.y[row] = p.r[row] + y;
+        p.y[row] = p.r ? p.r[row] + y : y;
     }
 }
 
@@ -571,6 +571,82 @@ hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+namespace {
+// The single-token head of a layer: one block per q, k or v head of the
+// stacked projection (gate heads are used as they are), one thread per
+// channel.  Bias, then the per-head Q/K RMS norm, then RoPE at position
+// p.pos ("frink-models 0.29.0 src/decoder/cuda_prefill.rs",
+// cuda_prefill_layer: the extras and the RoPE description -- the same order
+// as the prefill's QKV post-step); the rotation partner of a channel comes
+// through LDS.  Angles in fp64, then cos/sin times the attention factor in
+// fp32.
+template <int HD>
+__global__ __launch_bounds__(HD) void decode_head_kernel(DecodeHeadArgs p) {
+    __shared__ float xs[HD];
+    __shared__ float part[HD / 64];
+    const int slot = blockIdx.x, e = threadIdx.x;
+    const bool is_q = slot < p.hq, is_v = slot >= p.hq + p.hkv;
+    const int col = slot * HD + e;
+    float x = p.qkv[col];
+    if (p.bias) x += p.bias[col];
+    if (!is_v) {
+        const float* gn = is_q ? p.q_norm : p.k_norm;
+        if (gn) {
+            const float ss = wave_sum(x * x);
+            if ((e & 63) == 0) part[e >> 6] = ss;
+            __syncthreads();
+            float t = 0.f;
+#pragma unroll
+            for (int w = 0; w < HD / 64; ++w) t += part[w];
+            x = x * (1.0f / sqrtf(t / (float)HD + p.eps)) * gn[e];
+        }
+        if (p.rope_on) {
+            xs[e] = x;
+            __syncthreads();
+            const int rd = p.rot_dim, half = rd / 2;
+            if (e < rd) {
+                int i, partner;
+                bool first;
+                if (p.rope_layout == DDL_ROPE_NEOX) {
+                    first = e < half;
+                    i = first ? e : e - half;
+                    partner = first ? e + half : e - half;
+                } else {
+                    first = (e & 1) == 0;
+                    i = e >> 1;
+                    partner = e ^ 1;
+                }
+                double inv = pow(p.theta, -2.0 * (double)i / (double)rd);
+                if (p.freq) inv /= (double)p.freq[i];
+                const double ang = (double)p.pos * inv;
+                const float c = (float)(p.mscale * cos(ang)), sn = (float)(p.mscale * sin(ang));
+                const float xp = xs[partner];
+                // pair (a, b) -> (a c - b s, a s + b c)
+                x = first ? x * c - xp * sn : xp * sn + x * c;
+            }
+        }
+    }
+    if (is_q)
+        p.q[col] = x;
+    else if (!is_v)
+        p.k_row[(slot - p.hq) * HD + e] = x;
+    else
+        p.v_row[(slot - p.hq - p.hkv) * HD + e] = x;
+}
+}  // namespace
+
+hipError_t launch_decode_head(const DecodeHeadArgs& a, hipStream_t s) {
+    if (a.rope_on && (a.rot_dim < 2 || a.rot_dim % 2 || a.rot_dim > a.hd)) return hipErrorInvalidValue;
+    const dim3 grid(a.hq + 2 * a.hkv);
+    if (a.hd == 128)
+        hipLaunchKernelGGL(decode_head_kernel<128>, grid, dim3(128), 0, s, a);
+    else if (a.hd == 64)
+        hipLaunchKernelGGL(decode_head_kernel<64>, grid, dim3(64), 0, s, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 bool gemv_shape_ok(int K) { return K > 0 && K % 16 == 0 && K <= GV_MAXK; }
 
 hipError_t launch_gemv(const GemvArgs& a, int epi, hipStream_t s) {
@@ -582,7 +658,7 @@ hipError_t launch_gemv(const GemvArgs& a, int epi, hipStream_t s) {
     const size_t lds = a.K * sizeof(float);
     if (epi == GV_SWIGLU)
         hipLaunchKernelGGL((gemv_kernel<GV_SWIGLU, 1>), dim3(rows / 32), block, lds, s, a);
-    else if (rows / 32 < 256)   // fewer row blocks than CUs: 16-row halves
+    else if (rows / 32 < 512)   // under two rounds of row blocks on 256 CUs: 16-row halves
         hipLaunchKernelGGL((gemv_kernel<GV_RESID, 2>), dim3(rows / 16), block, lds, s, a);
     else
         hipLaunchKernelGGL((gemv_kernel<GV_RESID, 1>), dim3(rows / 32), block, lds, s, a);

@@ -205,9 +205,22 @@ struct GemvArgs {
     const float* inv_scale;      // device scalar
     const float* x;              // [K]
     const float* norm_g; float eps;   // RMS-norm x first when norm_g != null
-    const float* r;              // [N] residual (GV_RESID)
+    const float* r;              // [N] residual (GV_RESID; null: y = W x)
     float* y;                    // [N]
     int gelu;                    // GV_SWIGLU: gelu(gate) * up instead of silu(gate) * up
 };
 bool gemv_shape_ok(int K);
+
+// The single-token head: q/k/v heads of the stacked projection output ->
+// q [hq*hd], k_row, v_row [hkv*hd] (bias, Q/K norm, RoPE at pos).
+struct DecodeHeadArgs {
+    const float* qkv;                    // [nqkv] projection of the normed row
+    const float* bias;                   // [nqkv] or null
+    const float* q_norm; const float* k_norm;   // [hd] or null
+    float eps;
+    int rope_on, rope_layout, rot_dim; double theta; const float* freq; float mscale;
+    int pos, hq, hkv, hd;
+    float* q; float* k_row; float* v_row;
+};
+hipError_t launch_decode_head(const DecodeHeadArgs& a, hipStream_t s);
 hipError_t launch_gemv(const GemvArgs& a, int epi, hipStream_t s);

@@ -211,8 +211,8 @@ void ddl_mirror_invalidate(ddl_mirror* m);   /* seq_len = -1 */
 int ddl_mirror_plan_capacity(int rows, int planned);
 void ddl_mirror_destroy(ddl_mirror* m);
 
-/* Workspace bytes of ddl_attn_layer for a layer (the same for every row
- * count up to `capacity`). */
+/* Workspace bytes of ddl_attn_layer and ddl_decode_layer for a layer (the
+ * same for every row count up to `capacity`). */
 size_t ddl_attn_workspace_bytes(const ddl_layer* layer, int capacity);
 
 /* One token's attention layer in one submission against the mirror
@@ -238,6 +238,31 @@ int ddl_attn_layer(ddl_ctx* ctx, ddl_mirror* mirror, int host_rows,
                    const ddl_layer* layer, const float* residual, float* out,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* One token's whole decoder layer against the mirror, every step on the
+ * device: the head ([P1] cuda_prefill_layer's attention norm, stacked
+ * q/k/v(/gate) projection, extras and RoPE description) feeding the
+ * attention and tail of ddl_attn_layer -- the "one submission a layer" of
+ * [P3] (module doc, "Why") and [P2] device_attention_layer with q/k/v
+ * computed on the device instead of handed in.
+ *   host_rows  rows in the caller's host cache (the token's position);
+ *              declined unless the mirror's seq_len equals it and its
+ *              capacity is at least host_rows + 1
+ *   hidden     [d_model] fp32 (device): the layer input (also the residual)
+ *   out        [d_model] fp32 (device): the layer output; may alias hidden
+ *   k_row, v_row [n_kv_heads*head_dim] fp32 (device) out: this token's K row
+ *              (biased, QK-normed, rotated at position host_rows) and V row,
+ *              the rows the caller pushes into its host cache
+ *   workspace  >= ddl_attn_workspace_bytes(layer, capacity)
+ * The layer's softcap, gate, RoPE, extras and FFN activation are the packed
+ * layer's own.  Declines like ddl_attn_layer (and for the same layers).
+ * Returns 1 (served: the mirror holds the new row, seq_len = host_rows+1),
+ * 0 (declined, nothing touched) or < 0 (error: the mirror is marked
+ * stale). */
+int ddl_decode_layer(ddl_ctx* ctx, ddl_mirror* m, int host_rows,
+                     const float* hidden, const ddl_layer* layer, float* out,
+                     float* k_row, float* v_row, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 /* ---- launch timing probe (a measurement aid) -------------------------------
  * Kernel classes of the two operations. */
 enum {
@@ -252,7 +277,9 @@ enum {
     DDL_K_GEMV_WO = 8,
     DDL_K_GEMV_GATE_UP = 9,
     DDL_K_GEMV_DOWN = 10,
-    DDL_K_COUNT = 11
+    DDL_K_GEMV_QKV = 11,      /* decode head: RMS norm + stacked q/k/v(/gate) GEMV */
+    DDL_K_DECODE_HEAD = 12,   /* decode head: bias, QK norm, RoPE */
+    DDL_K_COUNT = 13
 };
 /* While enabled, each launch of class `kind` made through `ctx` is
  * bracketed by two HIP events recorded on the call's stream, for at most

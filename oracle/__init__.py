@@ -66,7 +66,7 @@ import numpy as np
 __all__ = [
     "rms_norm", "rope_angles", "apply_rope", "causal_gqa_attention", "silu", "gelu",
     "swiglu_ffn", "project_qkv", "dense_layer", "prefill_dense_stack",
-    "attn_layer", "kv_head_of",
+    "attn_layer", "decode_layer", "kv_head_of",
 ]
 
 F64 = np.float64
@@ -332,3 +332,23 @@ def attn_layer(q, k, v, gate, cache_k, cache_v, rows: int,
     h2 = rms_norm(x1, w["g_ffn"], spec.rms_eps)
     return x1 + swiglu_ffn(h2[None], w["wg"], w["wu"], w["wd"],
                            getattr(spec, "ffn_act", "swiglu"))[0]
+
+
+def decode_layer(x, w: Mapping[str, np.ndarray], spec, cache_k, cache_v, rows: int):
+    """One token's whole layer at position ``rows``: attention norm, the
+    q/k/v(/gate) projection with its extras and RoPE, then ``attn_layer``
+    over the ``rows`` cached rows plus this token's own.  Returns ``(out,
+    k_row, v_row)``; the rows are the ones the caller pushes into its cache.
+
+    fused_layer.rs (0.49.0), module doc ("Why": one submission a layer) and
+    device_attention.rs (0.38.0), ``device_attention_layer`` (q/k/v
+    post-RoPE and post-QK-norm feed the device attention); the head follows
+    cuda_prefill.rs (0.29.0), ``cuda_prefill_layer``.
+    """
+    x = _f64(x)
+    h = rms_norm(x[None], w["g_attn"], spec.rms_eps)
+    q, gate, k, v = project_qkv(h, w, spec, [rows])
+    out = attn_layer(q.reshape(-1), k.reshape(-1), v.reshape(-1),
+                     None if gate is None else gate.reshape(-1), cache_k, cache_v, rows, w,
+                     spec, x)
+    return out, k.reshape(-1), v.reshape(-1)

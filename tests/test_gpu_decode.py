@@ -214,3 +214,107 @@ def test_sandwich_norm_layer_is_declined_untouched(ddl):
     assert dec.step(cfg.rows, inp["q"], inp["k"], inp["v"], None, inp["residual"]) == 0
     assert "post" in ddl.ddl_last_error()
     assert ddl.ddl_mirror_seq_len(dec.mirror) == cfg.rows and torch.all(dec.out == 7.0)
+
+
+# ---------------------------------------------------------------------------
+# ddl_decode_layer: the whole single-token layer (head on the device)
+
+def dl_cfg(name, **kw):
+    base = dict(name=name, n_layers=1, d_model=512, n_heads=8, n_kv_heads=2, head_dim=128,
+                d_ff=1024, batch=1, start_pos=100, rope_theta=5e5, weight_dtype="bf16")
+    base.update(kw)
+    return synth.StackConfig(**base)
+
+
+DECODE_LAYER_CASES = {
+    "llama3b-rows1000-gated-softcap": synth.STACK_CONFIGS["llama3b_pp512"].replace(
+        n_layers=1, batch=1, start_pos=1000, gated=True, softcap=50.0),
+    "llama8b-extras-rows4096": synth.STACK_CONFIGS["llama8b_pp4096_extras"].replace(
+        n_layers=1, batch=1, start_pos=4096),
+    "all-options-rows77": dl_cfg("all-options-rows77", start_pos=77, qkv_bias=True, qk_norm=True,
+                                 gated=True, softcap=20.0, rope_layout="norm", rope_rot_dim=96,
+                                 rope_freq_factors=tuple(1.0 + 0.5 * i for i in range(48)),
+                                 rope_mscale=0.9, ffn_act="geglu"),
+    "mha-hd64-first-token": dl_cfg("mha-hd64-first-token", n_heads=4, n_kv_heads=4, head_dim=64,
+                                   start_pos=0, weight_dtype="fp32"),
+    "neox-rot64-rows300": dl_cfg("neox-rot64-rows300", rope_rot_dim=64, start_pos=300),
+}
+
+
+class DecodeLayer:
+    def __init__(self, ddl, cfg, planned=0):
+        from dense_decoder_layer_amd.workloads import desc_for
+        self.ddl, self.cfg = ddl, cfg
+        self.inp = synth.stack_inputs(cfg)
+        self.ctx = ddl.ddl_ctx_create()
+        self.layer = ddl.pack_layer_from_host(self.ctx, desc_for(cfg), self.inp.layers[0])
+        rows = cfg.start_pos
+        self.cap = ddl.ddl_mirror_plan_capacity(rows, planned)
+        self.buf = torch.empty(ddl.ddl_mirror_bytes(cfg.n_kv_heads, cfg.head_dim, self.cap),
+                               dtype=torch.uint8, device="cuda")
+        self.mirror = ddl.ddl_mirror_init(self.buf, cfg.n_kv_heads, cfg.head_dim, self.cap)
+        if rows:
+            assert ddl.ddl_mirror_upload(self.mirror, torch.from_numpy(self.inp.prefix_k[0]).cuda(),
+                                         torch.from_numpy(self.inp.prefix_v[0]).cuda(), rows) == 1
+        self.ws = torch.empty(ddl.ddl_attn_workspace_bytes(self.layer, self.cap),
+                              dtype=torch.uint8, device="cuda")
+        f32 = dict(dtype=torch.float32, device="cuda")
+        self.out = torch.empty(cfg.d_model, **f32)
+        self.k_row = torch.empty(cfg.kv_width, **f32)
+        self.v_row = torch.empty(cfg.kv_width, **f32)
+
+    def step(self, rows, x):
+        rc = self.ddl.ddl_decode_layer(self.ctx, self.mirror, rows,
+                                       torch.from_numpy(np.ascontiguousarray(x)).cuda(),
+                                       self.layer, self.out, self.k_row, self.v_row, self.ws)
+        torch.cuda.synchronize()
+        return rc
+
+    def mirror_row(self, r):
+        kvw = self.cfg.kv_width
+        flat = self.buf.view(torch.float32)
+        half = flat.numel() // 2
+        return (flat[r * kvw:(r + 1) * kvw].cpu().numpy(),
+                flat[half + r * kvw: half + (r + 1) * kvw].cpu().numpy())
+
+
+@pytest.mark.parametrize("name", list(DECODE_LAYER_CASES))
+def test_decode_layer_matches_oracle(ddl, name):
+    cfg = DECODE_LAYER_CASES[name]
+    say(f"[decode_layer {name}] rows={cfg.start_pos}")
+    dl = DecodeLayer(ddl, cfg)
+    rows, x = cfg.start_pos, dl.inp.hidden[0]
+    assert dl.step(rows, x) == 1
+    assert ddl.ddl_mirror_seq_len(dl.mirror) == rows + 1
+    w = {n: synth.values(a) for n, a in dl.inp.layers[0].items()}
+    ck = dl.inp.prefix_k[0] if rows else np.zeros((0, cfg.kv_width), np.float32)
+    cv = dl.inp.prefix_v[0] if rows else np.zeros((0, cfg.kv_width), np.float32)
+    want, wk, wv = oracle.decode_layer(x, w, cfg, ck, cv, rows)
+    got_k, got_v = dl.k_row.cpu().numpy(), dl.v_row.cpu().numpy()
+    err, ek, ev = rel(dl.out.cpu().numpy(), want), rel(got_k, wk), rel(got_v, wv)
+    say(f"  out rel L2 {err:.2e}  k_row {ek:.2e}  v_row {ev:.2e}")
+    assert err <= TOL and ek <= 5e-3 and ev <= 5e-3
+    mk, mv = dl.mirror_row(rows)            # the appended row is the returned row, bit for bit
+    np.testing.assert_array_equal(mk, got_k)
+    np.testing.assert_array_equal(mv, got_v)
+
+
+def test_decode_layer_chain_and_declines(ddl):
+    # two consecutive tokens: the second attends over the first one's row;
+    # a stale row count is declined with nothing touched
+    cfg = dl_cfg("chain", start_pos=40, gated=True, softcap=30.0, qk_norm=True)
+    dl = DecodeLayer(ddl, cfg)
+    w = {n: synth.values(a) for n, a in dl.inp.layers[0].items()}
+    ck, cv = dl.inp.prefix_k[0], dl.inp.prefix_v[0]
+    x0 = dl.inp.hidden[0]
+    x1 = np.random.default_rng(5).standard_normal(cfg.d_model).astype(np.float32)
+    assert dl.step(40, x0) == 1
+    k0, v0 = dl.k_row.cpu().numpy(), dl.v_row.cpu().numpy()
+    ck, cv = np.concatenate([ck, k0[None]]), np.concatenate([cv, v0[None]])
+    dl.out.fill_(7.0)
+    assert dl.step(40, x1) == 0 and "stale" in ddl.ddl_last_error()   # rows must be 41 now
+    assert torch.all(dl.out == 7.0) and ddl.ddl_mirror_seq_len(dl.mirror) == 41
+    assert dl.step(41, x1) == 1
+    want, wk, _ = oracle.decode_layer(x1, w, cfg, ck, cv, 41)
+    assert rel(dl.out.cpu().numpy(), want) <= TOL and rel(dl.k_row.cpu().numpy(), wk) <= 5e-3
+    assert ddl.ddl_mirror_seq_len(dl.mirror) == 42

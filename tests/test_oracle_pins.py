@@ -553,6 +553,26 @@ def test_decode_attn_layer_equals_prefill_of_one_token():
 # the input encoder
 
 
+@pytest.mark.parametrize("opts", [dict(), dict(qkv_bias=True, qk_norm=True, gated=True, softcap=3.0,
+                                             rope_layout="norm", rope_rot_dim=6,
+                                             rope_freq_factors=(1.0, 2.0, 8.0), rope_mscale=0.8,
+                                             ffn_act="geglu")])
+def test_decode_layer_equals_one_token_prefill(opts):
+    # the device-side decode layer (head + attention + tail) at position R is
+    # the prefill of one token over the R cached rows
+    spec = Spec(**opts)
+    w = rand_layer(spec)
+    R = 6
+    ck = RNG.standard_normal((R, spec.n_kv_heads * spec.head_dim))
+    cv = RNG.standard_normal((R, spec.n_kv_heads * spec.head_dim))
+    x = RNG.standard_normal(spec.d_model)
+    out, k_row, v_row = oracle.decode_layer(x, w, spec, ck, cv, R)
+    want, wk, wv = oracle.dense_layer(x[None], w, spec, R, ck, cv)
+    np.testing.assert_allclose(out, want[0], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(k_row, wk[0], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(v_row, wv[0], rtol=1e-13, atol=1e-14)
+
+
 def test_bf16_encoder_matches_torch_rne():
     x = (RNG.standard_normal(100000) * 0.02).astype(np.float32)
     x[:4] = [1.00390625, 1.01171875, -1.00390625, 0.0]   # exact ties round to even
