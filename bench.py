@@ -7,11 +7,13 @@ tokens/s, the stack's fraction of dense fp16/bf16 MFMA peak, the roofline of
 the dominant kernel (the gate/up projection + SwiGLU GEMM, timed per launch
 with HIP events in a second pass of the same steps), the single-token decode
 layer at 32768 cached rows (ms per layer, decode attention as a fraction of
-HBM bandwidth) and the CPU oracle timed on a bounded sample of the prefill
+HBM bandwidth), the other prefill workloads as secondary lines (the 3B stack
+over a 1536-row cached prefix, the 8B-shaped stack with biases and QK norms
+at pp4096) and the CPU oracle timed on a bounded sample of the prefill
 workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
-                    [--no-decode] [--copy-calibration]
+                    [--no-decode] [--no-secondary] [--copy-calibration]
 
 --copy-calibration adds three plain 1 GiB device-to-device copies at the end,
 the reference a hardware-counter run scales FETCH_SIZE / WRITE_SIZE by.
@@ -196,6 +198,66 @@ def decode_bench(ddl, ctx, reps=40):
             "tail": tail}
 
 
+def _time_stack(stack, hidden, start_pos, pk, pv, bufs, warmup, steps):
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        assert stack.run(hidden, start_pos, pk, pv, bufs) == len(stack.layers)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        stack.run(hidden, start_pos, pk, pv, bufs)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def _line(cfg, ms, steps, note):
+    flops, _ = algorithmic_flops(cfg)
+    return {"workload": f"{cfg.name}: {cfg.n_layers} layers, hidden {cfg.d_model}, "
+                        f"{cfg.n_heads} q / {cfg.n_kv_heads} KV heads x {cfg.head_dim}, "
+                        f"FFN {cfg.d_ff}, {cfg.batch} new tokens, start_pos {cfg.start_pos}" + note,
+            "tok_s": round(cfg.batch / (ms / 1e3), 1), "ms_per_step": round(ms, 3), "steps": steps,
+            "algorithmic_tflop_per_step": round(flops / 1e12, 3),
+            "mfma_peak_frac": round(flops / (ms / 1e3) / 1e12 / PEAK_MFMA_TFLOPS, 4)}
+
+
+def secondary_bench(ddl, ctx, stack3b, hidden3b, args):
+    """The other prefill workloads, each a whole stack per step with inputs
+    resident in HBM: the 3B stack over a 1536-row cached prefix per layer
+    (the same seeded weights as the headline, so the packed stack is reused),
+    and the 8B-shaped stack with q/k/v biases and QK norms at pp4096."""
+    import torch
+    import synth
+    from dense_decoder_layer_amd.workloads import DeviceStack
+    out = []
+    cfg = synth.STACK_CONFIGS["llama3b_prefix1536"]
+    pk, pv = [], []
+    for l in range(cfg.n_layers):
+        k, v = synth.prefix_rows(cfg, l)
+        pk.append(torch.from_numpy(k).cuda())
+        pv.append(torch.from_numpy(v).cuda())
+    bufs = stack3b.buffers(cfg.batch, cfg.start_pos)
+    steps = max(3, min(args.steps, 10))
+    ms = _time_stack(stack3b, hidden3b, cfg.start_pos, pk, pv, bufs, 2, steps)
+    log(f"3B over a 1536-row prefix: {ms:.3f} ms/step")
+    out.append(_line(cfg, ms, steps, "; prefix K/V rows fp32 resident per layer"))
+    del pk, pv, bufs
+    cfg = synth.STACK_CONFIGS["llama8b_pp4096_extras"]
+    t0 = time.time()
+    stack = DeviceStack(ctx, cfg, (synth.layer_weights(cfg, l) for l in range(cfg.n_layers)))
+    hidden = torch.from_numpy(synth.hidden_rows(cfg)).cuda()
+    bufs = stack.buffers(cfg.batch, 0)
+    log(f"packed the 8B stack in {time.time() - t0:.1f}s")
+    ms = _time_stack(stack, hidden, 0, None, None, bufs, 1, 3)
+    log(f"8B pp4096: {ms:.3f} ms/step")
+    out.append(_line(cfg, ms, 3, "; q/k/v biases and per-head QK RMSNorm"))
+    del stack, bufs, hidden
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -204,6 +266,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the other prefill workloads (3B over a 1536-row prefix, 8B pp4096)")
     ap.add_argument("--breakdown", action="store_true",
                     help="also time every prefill kernel class per launch (HIP events)")
     args = ap.parse_args()
@@ -292,6 +356,8 @@ def main():
     }
     if breakdown:
         result["breakdown"] = breakdown
+    if not args.no_secondary:
+        result["secondary"] = secondary_bench(ddl, ctx, stack, hidden, args)
     del stack, bufs
     torch.cuda.empty_cache()
     if not args.no_decode:
