@@ -146,10 +146,11 @@ template <int BM, int WN, int WGM, int WGN, int NS, int EPI, int NK>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p, int splits) {
     constexpr int NT = WGM * WGN * 64, BN = WN * WGN, WM = BM / WGM;
     constexpr int MI = WM / 32, NI = WN / 32;
-    constexpr int A_CH = BM * 8 / NT;               // 16-byte activation chunks per thread per k-tile
+    constexpr int A_TOT = BM * 8;                   // 16-byte activation chunks per k-tile
+    constexpr int A_CH = (A_TOT + NT - 1) / NT;     // per thread (six waves: the last one partial)
     constexpr int STAGE = BM * BK * 2;
     static_assert(MI >= 1 && NI >= 1, "wave tile below 32x32");
-    static_assert(A_CH >= 1 && A_CH * NT == BM * 8, "activation chunks split evenly");
+    static_assert(A_CH >= 1, "activation chunks");
     static_assert(NS >= 2 && NS <= 4, "pipeline depth");
     __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
@@ -167,9 +168,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p, int sp
     int a_dst[A_CH];                                // half8 index in an LDS slot
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
-        const int idx = i * NT + tid, r = idx >> 3, c = idx & 7;
+        const int idx = i * NT + tid;
+        const bool ok = A_CH * NT == A_TOT || idx < A_TOT;   // past the tile: loads row 0, never stored
+        const int r = ok ? idx >> 3 : 0, c = idx & 7;
         a_src[i] = p.A + (size_t)min(m0 + r, p.M - 1) * p.lda + (size_t)kt0 * BK + c * 8;   // rows past M: discarded outputs
-        a_dst[i] = r * 8 + (c ^ (r & 7));
+        a_dst[i] = ok ? r * 8 + (c ^ (r & 7)) : -1;
     }
     const f16* wfrag[NI];
 #pragma unroll
@@ -193,7 +196,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p, int sp
         constexpr int slot = decltype(slot_c)::value;
         half8* As = reinterpret_cast<half8*>(smem + buf * STAGE);
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i) As[a_dst[i]] = areg[slot][i];
+        for (int i = 0; i < A_CH; ++i)
+            if (A_CH * NT == A_TOT || a_dst[i] >= 0) As[a_dst[i]] = areg[slot][i];
     };
 
     floatx16 acc[MI][NI];
@@ -270,6 +274,7 @@ hipError_t launch_cfg(const GemmArgs& a, int splits, hipStream_t s) {
 template <int BM, int WN, int WGM, int WGN, int NS, int EPI>
 hipError_t launch_nk(const GemmArgs& a, int splits, hipStream_t s) {
     switch (a.K / BK / splits) {
+        case 16: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 16>(a, splits, s);
         case 24: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 24>(a, splits, s);
         case 32: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 32>(a, splits, s);
         case 48: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 48>(a, splits, s);
@@ -286,21 +291,27 @@ bool gemm_shape_ok(int M, int N, int K, int epi) {
     return M > 0 && N > 0 && K > 0 && N % 128 == 0 && K % BK == 0;
 }
 
-// Tiles and K splits (measured on MI355X at the 512-token shapes).
-//  * gate/up and the stacked QKV projection, N a multiple of 256 and more
-//    than 64 rows: 128 x 256 tiles, eight waves of 128 x 32 sharing one
-//    activation tile (a third fewer bytes per flop than two 128 x 128
-//    workgroups on a CU), 3-deep register prefetch; one workgroup per CU.
-//    gate/up is not split (SwiGLU needs the whole sum); QKV has 80 such
-//    tiles and splits K in two (160 workgroups beat 640 smaller ones).
-//  * The residual projections take 64 x 128 tiles (four waves of 64 x 32,
-//    three workgroups fit a CU) and split K until the grid fills the 768
-//    workgroup slots, each slice keeping at least 24 k-tiles.  Where K is
-//    too short for a four-way split (wo), 64 x 256 tiles of eight waves
-//    with a two-way split are faster than more, smaller workgroups.
+// Tiles and K splits (measured on MI355X at the 512-token shapes).  At
+// these shapes the narrow projections are limited by how many CUs their grid
+// fills, so the plan aims at one 8- or 6-wave workgroup per CU:
+//  * gate/up: 128 x 256 tiles, eight waves of 128 x 32 sharing one
+//    activation tile, 3-deep register prefetch (a third fewer bytes per flop
+//    than two 128 x 128 workgroups on a CU).  Never split (SwiGLU/GELU need
+//    the whole sum).
+//  * stacked QKV: the same tile, K split so the grid comes closest to 256
+//    workgroups (80 tiles at 512 tokens: three slices, 240 workgroups; 23 us
+//    against 28 us with two).
+//  * wo and down, width a multiple of 192: 64 x 192 tiles of six waves,
+//    split to fill 256 workgroups (two slices at 512 tokens).  For down this
+//    matches the four-way split of 64 x 128 tiles in time with one partial
+//    sum instead of three for the next norm to add.
+//  * other residual shapes: 64 x 128 tiles (four waves, three workgroups fit
+//    a CU) split until 768 workgroup slots fill, each slice keeping at least
+//    24 k-tiles; 64 x 256 tiles of eight waves where that gives fewer than
+//    four slices.
 //  * Anything else: 64 x 128 tiles, gate/up 128 x 128.
 namespace {
-enum Tile { T64x128, T128x128, T128x256, T64x256 };
+enum Tile { T64x128, T128x128, T128x256, T64x256, T64x192 };
 struct Plan {
     Tile tile;
     int splits;
@@ -314,11 +325,22 @@ int split_count(int tiles, int slots, int nk) {
     return splits;
 }
 
+// The K split in 1..4 that brings tiles * split closest to `slots` without
+// passing it, each slice keeping at least 16 k-tiles.
+int fill_split(int tiles, int slots, int nk) {
+    int best = 1;
+    for (int s = 2; s <= 4; ++s)
+        if (tiles * s <= slots && nk % s == 0 && nk / s >= 16) best = s;
+    return best;
+}
+
 Plan gemm_plan(int M, int N, int K, int epi) {
     const int nk = K / BK;
     if (epi == EPI_SWIGLU || epi == EPI_GEGLU) return {N % 256 == 0 && M > 64 ? T128x256 : T128x128, 1};
     if (epi == EPI_F32 && N % 256 == 0 && M > 64)
-        return {T128x256, split_count(((M + 127) / 128) * (N / 256), 256, nk)};
+        return {T128x256, fill_split(((M + 127) / 128) * (N / 256), 256, nk)};
+    if (epi == EPI_RESID && N % 192 == 0 && M > 64 && ((M + 63) / 64) * (N / 192) <= 256)
+        return {T64x192, fill_split(((M + 63) / 64) * (N / 192), 256, nk)};
     const int splits = split_count(((M + 63) / 64) * (N / 128), 768, nk);
     if (epi == EPI_RESID && splits < 4 && N % 256 == 0)
         return {T64x256, split_count(((M + 63) / 64) * (N / 256), 256, nk)};
@@ -348,6 +370,7 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, int splits, hipStream_t s) {
             if (t == T128x256) return launch_nk<128, 32, 1, 8, 3, EPI_F32>(a, splits, s);
             return launch_nk<64, 32, 1, 4, 4, EPI_F32>(a, splits, s);
         case EPI_RESID:
+            if (t == T64x192) return launch_nk<64, 32, 1, 6, 3, EPI_RESID>(a, splits, s);
             if (t == T64x256) return launch_nk<64, 32, 1, 8, 3, EPI_RESID>(a, splits, s);
             return launch_nk<64, 32, 1, 4, 4, EPI_RESID>(a, splits, s);
     }
