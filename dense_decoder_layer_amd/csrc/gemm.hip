@@ -8,7 +8,9 @@
 // matmul that produces their input):
 //   EPI_F32     store fp32 (the stacked q/k/v/gate projection)
 //   EPI_RESID   C = R + acc (wo and down projections plus the residual;
-//               with R null, C = acc for a layer whose branch is normed first)
+//               with R null, C = acc for a layer whose branch is normed first).
+//               The residual tile is read before the k-loop (9 us of exposed
+//               latency per launch when read in the epilogue)
 //   EPI_SWIGLU  W rows are gate/up interleaved in 16-row blocks; store
 //               fp16 silu(gate) * up into H[M][N/2]
 //   EPI_GEGLU   the same with the exact GELU, gate * Phi(gate), in place of
@@ -72,9 +74,38 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // Accumulator layout of a 32x32 MFMA tile: lane l holds column l % 32 of
 // rows 8*(e/4) + 4*(l/32) + e%4 for e = 0..15.
+// The residual tile of a wave (EPI_RESID, K slice 0), read into registers
+// before the k-loop so its memory latency hides behind the MFMAs instead of
+// being exposed at the end (R may alias C: each element is read and written
+// by the same lane, and no other workgroup writes this tile of C).
+template <int MI, int NI, int EPI>
+struct ResidTile {
+    float v[EPI == EPI_RESID ? MI : 1][EPI == EPI_RESID ? NI : 1][16];
+};
+
+template <int MI, int NI, int EPI>
+__device__ __forceinline__ void load_resid(const GemmArgs& p, ResidTile<MI, NI, EPI>& rt, int row0,
+                                           int col0, int lane, bool full, int split) {
+    if constexpr (EPI == EPI_RESID) {
+        const int rbase = row0 + 4 * (lane >> 5), cl = lane & 31;
+        const bool use = split == 0 && p.R;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
+                    rt.v[i][j][e] = use && (full || row < p.M)
+                                        ? p.R[(size_t)row * p.ldr + col0 + j * 32 + cl] : 0.f;
+                }
+    }
+}
+
 template <int MI, int NI, int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, floatx16 (&acc)[MI][NI], int row0,
-                                         int col0, int lane, bool full, int split) {
+                                         int col0, int lane, bool full, int split,
+                                         const ResidTile<MI, NI, EPI>& rt) {
     const float sc = *p.inv_scale;
     const int rbase = row0 + 4 * (lane >> 5);
     const int cl = lane & 31;
@@ -122,13 +153,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, floatx16 (&acc)[MI][
                     }
                     continue;
                 }
-                if constexpr (EPI == EPI_RESID) {
-                    if (p.R)   // null: the raw branch output (a sandwich norm follows)
+                if constexpr (EPI == EPI_RESID) {   // zeros when R is null (raw branch output)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
-                        if (full || row < p.M) v[e] += p.R[(size_t)row * p.ldr + col];
-                    }
+                    for (int e = 0; e < 16; ++e) v[e] += rt.v[i][j][e];
                 }
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
@@ -241,6 +268,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p, int sp
         lds_barrier();
     };
 
+    ResidTile<MI, NI, EPI> rt;
+    load_resid<MI, NI, EPI>(p, rt, m0 + wm * WM, n0 + wn * WN, lane, m0 + BM <= p.M, split);
     issue(0, std::integral_constant<int, 0>());
     if constexpr (NS > 2) issue(min(1, nk - 1), std::integral_constant<int, 1>());
     if constexpr (NS > 3) issue(min(2, nk - 1), std::integral_constant<int, 2>());
@@ -259,7 +288,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p, int sp
             if constexpr (NS > 3) if (kt + 3 < nk) step(kt + 3, std::integral_constant<int, 3 % NS>());
         }
     }
-    epilogue<MI, NI, EPI>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, m0 + BM <= p.M, split);
+    epilogue<MI, NI, EPI>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, m0 + BM <= p.M, split, rt);
 }
 
 template <int BM, int WN, int WGM, int WGN, int NS, int EPI, int NK>
