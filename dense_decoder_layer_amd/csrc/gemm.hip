@@ -31,6 +31,8 @@
 //    of 8 consecutive lanes (one row each, same chunk) hit distinct banks.
 //    Every load of the kernel is an ordinary register load, so the
 //    hardware returns them in issue order and one counter tracks them.
+//  * A stage spans 64 k (128 for the six-wave 64 x 192 tiles, where
+//    halving the barriers per K measured 11-21% faster).
 //  * Per k-tile: issue the loads of k-tile kt+NS-1, multiply k-tile kt,
 //    write k-tile kt+1's activations into the other LDS slot, barrier.
 //    For the K of the hot projections the k-loop is unrolled at compile
@@ -47,7 +49,7 @@ namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int BK = 64;   // k per pipeline stage
+constexpr int BK = 64;   // k granularity of the shapes; a kernel's stage takes BKT = 64 or 128
 
 __device__ __forceinline__ floatx16 mfma32x32x16(half8 a, half8 b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -169,13 +171,14 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, floatx16 (&acc)[MI][
 // Workgroup of WGM x WGN waves, tile BM x (WN*WGN); wave tile (BM/WGM) x WN.
 // The grid is tiles x splits; slice z takes k-tiles [z*nk, (z+1)*nk).
 // NK > 0: nk == NK, straight-line k-loop; NK == 0: generic loop.
-template <int BM, int WN, int WGM, int WGN, int NS, int EPI, int NK>
+template <int BM, int WN, int WGM, int WGN, int NS, int EPI, int NK, int BKT>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p, int splits) {
+    constexpr int KC = BKT / 8;                     // 16-byte chunks per activation row of a stage
     constexpr int NT = WGM * WGN * 64, BN = WN * WGN, WM = BM / WGM;
     constexpr int MI = WM / 32, NI = WN / 32;
-    constexpr int A_TOT = BM * 8;                   // 16-byte activation chunks per k-tile
+    constexpr int A_TOT = BM * KC;                  // 16-byte activation chunks per k-tile
     constexpr int A_CH = (A_TOT + NT - 1) / NT;     // per thread (six waves: the last one partial)
-    constexpr int STAGE = BM * BK * 2;
+    constexpr int STAGE = BM * BKT * 2;
     static_assert(MI >= 1 && NI >= 1, "wave tile below 32x32");
     static_assert(A_CH >= 1, "activation chunks");
     static_assert(NS >= 2 && NS <= 4, "pipeline depth");
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p, int sp
     if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
     const int tile = bid % (mt * nt), split = bid / (mt * nt);
     const int m0 = (tile % mt) * BM, n0 = (tile / mt) * BN;
-    const int nk = NK > 0 ? NK : p.K / BK / splits;
+    const int nk = NK > 0 ? NK : p.K / BKT / splits;
     const int kt0 = split * nk;                    // this slice's first k-tile
 
     const f16* a_src[A_CH];
@@ -197,27 +200,27 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p, int sp
     for (int i = 0; i < A_CH; ++i) {
         const int idx = i * NT + tid;
         const bool ok = A_CH * NT == A_TOT || idx < A_TOT;   // past the tile: loads row 0, never stored
-        const int r = ok ? idx >> 3 : 0, c = idx & 7;
-        a_src[i] = p.A + (size_t)min(m0 + r, p.M - 1) * p.lda + (size_t)kt0 * BK + c * 8;   // rows past M: discarded outputs
-        a_dst[i] = ok ? r * 8 + (c ^ (r & 7)) : -1;
+        const int r = ok ? idx / KC : 0, c = idx % KC;
+        a_src[i] = p.A + (size_t)min(m0 + r, p.M - 1) * p.lda + (size_t)kt0 * BKT + c * 8;   // rows past M: discarded outputs
+        a_dst[i] = ok ? r * KC + (c ^ (r & 7)) : -1;
     }
     const f16* wfrag[NI];
 #pragma unroll
     for (int j = 0; j < NI; ++j)
-        wfrag[j] = p.W + ((size_t)((n0 + wn * WN) / 32 + j) * (p.K / 16) + (size_t)kt0 * 4) * 512 + lane * 8;
+        wfrag[j] = p.W + ((size_t)((n0 + wn * WN) / 32 + j) * (p.K / 16) + (size_t)kt0 * (BKT / 16)) * 512 + lane * 8;
 
     half8 areg[NS][A_CH];
-    half8 breg[NS][NI][BK / 16];
+    half8 breg[NS][NI][BKT / 16];
     auto issue = [&](int kt, auto slot_c) {
         constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
         for (int i = 0; i < A_CH; ++i)
-            areg[slot][i] = *reinterpret_cast<const half8*>(a_src[i] + (size_t)kt * BK);
+            areg[slot][i] = *reinterpret_cast<const half8*>(a_src[i] + (size_t)kt * BKT);
 #pragma unroll
         for (int j = 0; j < NI; ++j)
 #pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks)
-                breg[slot][j][ks] = *reinterpret_cast<const half8*>(wfrag[j] + (size_t)(kt * 4 + ks) * 512);
+            for (int ks = 0; ks < BKT / 16; ++ks)
+                breg[slot][j][ks] = *reinterpret_cast<const half8*>(wfrag[j] + (size_t)(kt * (BKT / 16) + ks) * 512);
     };
     auto commit = [&](auto slot_c, int buf) {
         constexpr int slot = decltype(slot_c)::value;
@@ -247,15 +250,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p, int sp
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
             const int r = wm * WM + i * 32 + (lane & 31), c = lane >> 5;
-            af[0][i] = As[r * 8 + (c ^ (r & 7))];
+            af[0][i] = As[r * KC + (c ^ (r & 7))];
         }
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            if (ks + 1 < BK / 16) {
+        for (int ks = 0; ks < BKT / 16; ++ks) {
+            if (ks + 1 < BKT / 16) {
 #pragma unroll
                 for (int i = 0; i < MI; ++i) {
                     const int r = wm * WM + i * 32 + (lane & 31), c = (ks + 1) * 2 + (lane >> 5);
-                    af[(ks + 1) & 1][i] = As[r * 8 + (c ^ (r & 7))];
+                    af[(ks + 1) & 1][i] = As[r * KC + (c ^ (r & 7))];
                 }
             }
 #pragma unroll
@@ -291,25 +294,27 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p, int sp
     epilogue<MI, NI, EPI>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, m0 + BM <= p.M, split, rt);
 }
 
-template <int BM, int WN, int WGM, int WGN, int NS, int EPI, int NK>
+template <int BM, int WN, int WGM, int WGN, int NS, int EPI, int NK, int BKT>
 hipError_t launch_cfg(const GemmArgs& a, int splits, hipStream_t s) {
     const int mt = (a.M + BM - 1) / BM, nt = a.N / (WN * WGN);
-    hipLaunchKernelGGL((gemm_kernel<BM, WN, WGM, WGN, NS, EPI, NK>), dim3(mt * nt * splits),
+    hipLaunchKernelGGL((gemm_kernel<BM, WN, WGM, WGN, NS, EPI, NK, BKT>), dim3(mt * nt * splits),
                        dim3(WGM * WGN * 64), 0, s, a, splits);
     return hipGetLastError();
 }
 
 // The k-tile counts per slice of the hot shapes get the straight-line loop.
-template <int BM, int WN, int WGM, int WGN, int NS, int EPI>
+template <int BM, int WN, int WGM, int WGN, int NS, int EPI, int BKT = 64>
 hipError_t launch_nk(const GemmArgs& a, int splits, hipStream_t s) {
-    switch (a.K / BK / splits) {
-        case 16: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 16>(a, splits, s);
-        case 24: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 24>(a, splits, s);
-        case 32: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 32>(a, splits, s);
-        case 48: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 48>(a, splits, s);
-        case 64: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 64>(a, splits, s);
-        case 128: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 128>(a, splits, s);
-        default: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 0>(a, splits, s);
+    switch (a.K / BKT / splits) {
+        case 8: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 8, BKT>(a, splits, s);
+        case 12: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 12, BKT>(a, splits, s);
+        case 16: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 16, BKT>(a, splits, s);
+        case 24: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 24, BKT>(a, splits, s);
+        case 32: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 32, BKT>(a, splits, s);
+        case 48: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 48, BKT>(a, splits, s);
+        case 64: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 64, BKT>(a, splits, s);
+        case 128: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 128, BKT>(a, splits, s);
+        default: return launch_cfg<BM, WN, WGM, WGN, NS, EPI, 0, BKT>(a, splits, s);
     }
 }
 
@@ -399,7 +404,9 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, int splits, hipStream_t s) {
             if (t == T128x256) return launch_nk<128, 32, 1, 8, 3, EPI_F32>(a, splits, s);
             return launch_nk<64, 32, 1, 4, 4, EPI_F32>(a, splits, s);
         case EPI_RESID:
-            if (t == T64x192) return launch_nk<64, 32, 1, 6, 3, EPI_RESID>(a, splits, s);
+            if (t == T64x192)   // 128-wide k stages where a slice divides (wo 24 -> 19 us, down 41 -> 36 us in a harness)
+                return (a.K / splits) % 128 == 0 ? launch_nk<64, 32, 1, 6, 3, EPI_RESID, 128>(a, splits, s)
+                                                 : launch_nk<64, 32, 1, 6, 3, EPI_RESID>(a, splits, s);
             if (t == T64x256) return launch_nk<64, 32, 1, 8, 3, EPI_RESID>(a, splits, s);
             return launch_nk<64, 32, 1, 4, 4, EPI_RESID>(a, splits, s);
     }
