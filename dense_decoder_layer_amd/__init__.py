@@ -87,7 +87,8 @@ class Ctx:
         self.handle = handle
 
     def __del__(self):
-        if getattr(self, "handle", None):
+        # at interpreter exit the module's globals may already be gone
+        if getattr(self, "handle", None) and ddl_ctx_destroy is not None:
             ddl_ctx_destroy(self)
 
 
@@ -143,7 +144,8 @@ class Layer:
         self.handle, self.blob, self.desc = handle, blob, desc
 
     def __del__(self):
-        if getattr(self, "handle", None):
+        # at interpreter exit the module's globals may already be gone
+        if getattr(self, "handle", None) and ddl_layer_destroy is not None:
             ddl_layer_destroy(self)
 
 
@@ -235,7 +237,8 @@ class Mirror:
         self.handle, self.buf = handle, buf
 
     def __del__(self):
-        if getattr(self, "handle", None):
+        # at interpreter exit the module's globals may already be gone
+        if getattr(self, "handle", None) and ddl_mirror_destroy is not None:
             ddl_mirror_destroy(self)
 
 
