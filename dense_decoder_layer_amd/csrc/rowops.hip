@@ -280,10 +280,21 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs p) {
         vt[e + 3][tl] = (f16)x[i].w;
     }
     __syncthreads();
-    // row e of Vt16 gets this block's 32 keys
-    for (int idx = tid; idx < HD * 32; idx += 256) {
-        const int e = idx >> 5, t = idx & 31;
-        p.vt16[((size_t)g * HD + e) * p.tcap + p.S + blk * 32 + t] = vt[e][t];
+    // row e of Vt16 gets this block's 32 keys: 16-byte stores of 8 keys when
+    // the block's first key is 8-aligned, else one key at a time
+    if ((p.S & 7) == 0) {
+        for (int idx = tid; idx < HD * 4; idx += 256) {
+            const int e = idx >> 2, t0 = (idx & 3) * 8;
+            half8 w;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) w[u] = vt[e][t0 + u];
+            *reinterpret_cast<half8*>(p.vt16 + ((size_t)g * HD + e) * p.tcap + p.S + blk * 32 + t0) = w;
+        }
+    } else {
+        for (int idx = tid; idx < HD * 32; idx += 256) {
+            const int e = idx >> 5, t = idx & 31;
+            p.vt16[((size_t)g * HD + e) * p.tcap + p.S + blk * 32 + t] = vt[e][t];
+        }
     }
 }
 
