@@ -82,13 +82,19 @@ void ddl_ctx_destroy(ddl_ctx* ctx);
  * and the attention parameters; [P2] device_attention_shape_ok).  Every
  * field must be answered: a layer with anything the kernels do not
  * implement is declined, never silently dropped ([P3] "What it refuses").
- *   served: act == DDL_ACT_SWIGLU; post_norm_eps == rms_eps; v_head_dim ==
- *   head_dim; window == 0; no post-attention/post-FFN norm, sinks, ALiBi or
- *   LoRA; rope either disabled or Neox with rot_dim == head_dim, mscale == 1
- *   and no frequency factors; head_dim in {64, 128}; n_heads a multiple of
+ *   served: act DDL_ACT_SWIGLU or DDL_ACT_GELU (gated GELU, exact erf form;
+ *   [P1] try_cuda_prefill_dense_stack names it); post_norm_eps == rms_eps;
+ *   v_head_dim == head_dim; window >= 0 (0 = none; W > 0: the token at
+ *   position p sees keys p-W+1 .. p); post-attention / post-FFN (sandwich)
+ *   norms; no sinks, ALiBi or LoRA; rope disabled, or Neox / Norm layout
+ *   with rot_dim (0 = head_dim) even and at most head_dim -- for Neox a
+ *   multiple of 64 -- any positive frequency factors ([rot_dim/2], host,
+ *   copied at pack time) and any finite attention factor mscale (on the
+ *   rotated channels); head_dim in {64, 128}; n_heads a multiple of
  *   n_kv_heads; d_model a multiple of 128 and at most 4096; d_ff a multiple
  *   of 64; the stacked q/k/v(/gate) width a multiple of 128; softcap >= 0.
- *   ddl_attn_layer further needs n_heads / n_kv_heads in {1, 2, 3, 4, 8}
+ *   ddl_attn_layer and ddl_decode_layer further need n_heads / n_kv_heads
+ *   in {1, 2, 3, 4, 8}, no window and no sandwich norms
  *   and d_model, d_ff, n_heads*head_dim at most 15872 (declined otherwise). */
 typedef struct {
     int d_model, n_heads, n_kv_heads, head_dim, v_head_dim, d_ff;
