@@ -266,3 +266,48 @@ def test_llama8b_pp4096_extras_first_layers(ddl):
     # the whole 32-layer stack is ~57 TFLOP of fp64 oracle work; the first
     # two layers at the full pp4096 shape keep the check within minutes
     _full_case(ddl, "llama8b_pp4096_extras", synth.STACK_CONFIGS["llama8b_pp4096_extras"], 2)
+
+
+def test_run_of_layers_with_different_options(ddl):
+    # one run whose layers differ in everything that is per layer: RoPE
+    # (Neox theta 5e5 / Norm theta 1e4 over 64 channels with factors / none),
+    # FFN activation, window, softcap, sandwich norms.  The position
+    # table is rebuilt whenever the RoPE description changes.  A fourth layer
+    # with another rms_eps ends the run.
+    base = small("mixed", n_layers=1, batch=70, start_pos=0, d_model=512, n_heads=8, n_kv_heads=2,
+                 head_dim=128, d_ff=1024)
+    cfgs = [base,
+            base.replace(rope_layout="norm", rope_theta=1e4, rope_rot_dim=64,
+                         rope_freq_factors=tuple(1.0 + 0.1 * i for i in range(32)),
+                         ffn_act="geglu", window=20, softcap=15.0, post_norms=True),
+            base.replace(rope_theta=None, gated=False, window=0, qk_norm=False),
+            base.replace(rms_eps=1e-6)]
+    from dense_decoder_layer_amd.workloads import desc_for
+    ctx = ddl.ddl_ctx_create(min_batch=1)
+    layers, host = [], []
+    for i, c in enumerate(cfgs):
+        w = synth.layer_weights(c.replace(seed=i), 0)
+        host.append(w)
+        layers.append(ddl.pack_layer_from_host(ctx, desc_for(c), w))
+    B, kvw = base.batch, base.kv_width
+    x = synth.hidden_rows(base)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    out = torch.empty(B, base.d_model, **f32)
+    ks = [torch.full((B, kvw), 7.0, **f32) for _ in cfgs]
+    vs = [torch.full((B, kvw), 7.0, **f32) for _ in cfgs]
+    ws = torch.empty(ddl.ddl_workspace_bytes(layers, B, 0), dtype=torch.uint8, device="cuda")
+    run = ddl.ddl_prefill_dense_stack(ctx, torch.from_numpy(x).cuda(), layers, 0, None, None,
+                                      [0] * len(cfgs), out, ks, vs, ws)
+    torch.cuda.synchronize()
+    assert run == 3, ddl.ddl_last_error()
+    assert bool((ks[3] == 7.0).all())                 # the fourth layer did not run
+    want = np.asarray(x, np.float64)
+    for l in range(3):
+        w = {n: synth.values(a) for n, a in host[l].items()}
+        want, wk, wv = oracle.dense_layer(want, w, cfgs[l], 0)
+        ek, ev = rel(ks[l].cpu().numpy(), wk), rel(vs[l].cpu().numpy(), wv)
+        say(f"[mixed] layer {l}: K {ek:.2e} V {ev:.2e}")
+        assert ek <= KV_TOL and ev <= KV_TOL
+    err = rel(out.cpu().numpy(), want)
+    say(f"[mixed] hidden after 3 layers: {err:.2e}")
+    assert err <= HIDDEN_TOL
