@@ -175,3 +175,26 @@ def test_oracle_and_gpu_path_share_no_code():
         if f.endswith(".py"):
             mods = import_re.findall(open(os.path.join(ROOT, "synth", f)).read())
             assert not any(m.split(".")[0] in ("dense_decoder_layer_amd", "oracle") for m in mods)
+
+
+def test_build_works_in_a_checkout_without_the_library(tmp_path):
+    # __graft_entry__.build() must build before it imports the package (which
+    # refuses to load without the library).  In a copy of the tree without
+    # libddl.so, a stand-in build script places the library built here
+    # (compiling again would take minutes).
+    import shutil
+    import sys as _sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    lib = os.path.join(root, "dense_decoder_layer_amd", "libddl.so")
+    shutil.copy(os.path.join(root, "__graft_entry__.py"), tmp_path)
+    shutil.copytree(os.path.join(root, "dense_decoder_layer_amd"), tmp_path / "dense_decoder_layer_amd",
+                    ignore=shutil.ignore_patterns("*.so", "_build", "__pycache__", "csrc"))
+    assert not (tmp_path / "dense_decoder_layer_amd" / "libddl.so").exists()
+    (tmp_path / "dense_decoder_layer_amd" / "build.py").write_text(
+        "import os, shutil\n"
+        "def build(verbose=False):\n"
+        f"    shutil.copy({lib!r}, os.path.join(os.path.dirname(os.path.abspath(__file__)), 'libddl.so'))\n")
+    r = subprocess.run([_sys.executable, "-c", "import __graft_entry__ as g; g.build()"], cwd=tmp_path,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert (tmp_path / "dense_decoder_layer_amd" / "libddl.so").exists()
