@@ -55,11 +55,14 @@ def cpu_baseline(cfg, budget_s=12.0):
     drawing the inputs is not timed.  Scaled to the whole stack."""
     import oracle
     import synth
+    # the threads the oracle actually runs on: its matrix products use the
+    # BLAS pool (OMP_NUM_THREADS, the host's CPU share for one GPU); its
+    # elementwise steps run on one thread
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        cores = os.cpu_count() or 1
+        cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
     x = synth.hidden_rows(cfg)
     spent, done = 0.0, 0
     while done < cfg.n_layers and spent < budget_s:
@@ -70,7 +73,7 @@ def cpu_baseline(cfg, budget_s=12.0):
         done += 1
     per_step = spent * cfg.n_layers / done
     return {"value": round(cfg.batch / per_step, 2), "unit": "tok/s", "cores": cores,
-            "kind": "oracle",
+            "host_nproc": os.cpu_count(), "kind": "oracle",
             "sample": f"first {done} of {cfg.n_layers} layers at pp{cfg.batch} "
                       f"(fp64 numpy oracle, {spent:.1f}s), scaled x{cfg.n_layers / done:g}"}
 
@@ -198,27 +201,41 @@ def decode_bench(ddl, ctx, reps=40):
             "tail": tail}
 
 
-def _time_stack(stack, hidden, start_pos, pk, pv, bufs, warmup, steps):
+def timed_steps(step, steps):
+    """Runs `step` `steps` times back to back on the current stream, with an
+    event between consecutive steps (no synchronisation inside the timed
+    region).  Returns (mean, median, min) ms per step; the mean is the
+    whole span over the step count."""
+    import statistics
     import torch
     stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return ev[0].elapsed_time(ev[steps]) / steps, statistics.median(per), min(per)
+
+
+def _time_stack(stack, hidden, start_pos, pk, pv, bufs, warmup, steps):
+    import torch
     for _ in range(warmup):
         assert stack.run(hidden, start_pos, pk, pv, bufs) == len(stack.layers)
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
-        stack.run(hidden, start_pos, pk, pv, bufs)
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    return timed_steps(lambda: stack.run(hidden, start_pos, pk, pv, bufs), steps)
 
 
-def _line(cfg, ms, steps, note):
+def _line(cfg, times, steps, note):
     flops, _ = algorithmic_flops(cfg)
+    ms, med, mn = times
     return {"workload": f"{cfg.name}: {cfg.n_layers} layers, hidden {cfg.d_model}, "
                         f"{cfg.n_heads} q / {cfg.n_kv_heads} KV heads x {cfg.head_dim}, "
                         f"FFN {cfg.d_ff}, {cfg.batch} new tokens, start_pos {cfg.start_pos}" + note,
-            "tok_s": round(cfg.batch / (ms / 1e3), 1), "ms_per_step": round(ms, 3), "steps": steps,
+            "tok_s": round(cfg.batch / (ms / 1e3), 1), "ms_per_step": round(ms, 3),
+            "ms_median": round(med, 3), "ms_min": round(mn, 3), "steps": steps,
             "algorithmic_tflop_per_step": round(flops / 1e12, 3),
             "mfma_peak_frac": round(flops / (ms / 1e3) / 1e12 / PEAK_MFMA_TFLOPS, 4)}
 
@@ -240,9 +257,9 @@ def secondary_bench(ddl, ctx, stack3b, hidden3b, args):
         pv.append(torch.from_numpy(v).cuda())
     bufs = stack3b.buffers(cfg.batch, cfg.start_pos)
     steps = max(3, min(args.steps, 10))
-    ms = _time_stack(stack3b, hidden3b, cfg.start_pos, pk, pv, bufs, 2, steps)
-    log(f"3B over a 1536-row prefix: {ms:.3f} ms/step")
-    out.append(_line(cfg, ms, steps, "; prefix K/V rows fp32 resident per layer"))
+    times = _time_stack(stack3b, hidden3b, cfg.start_pos, pk, pv, bufs, 2, steps)
+    log(f"3B over a 1536-row prefix: {times[0]:.3f} ms/step")
+    out.append(_line(cfg, times, steps, "; prefix K/V rows fp32 resident per layer"))
     del pk, pv, bufs
     cfg = synth.STACK_CONFIGS["llama8b_pp4096_extras"]
     t0 = time.time()
@@ -250,9 +267,9 @@ def secondary_bench(ddl, ctx, stack3b, hidden3b, args):
     hidden = torch.from_numpy(synth.hidden_rows(cfg)).cuda()
     bufs = stack.buffers(cfg.batch, 0)
     log(f"packed the 8B stack in {time.time() - t0:.1f}s")
-    ms = _time_stack(stack, hidden, 0, None, None, bufs, 1, 3)
-    log(f"8B pp4096: {ms:.3f} ms/step")
-    out.append(_line(cfg, ms, 3, "; q/k/v biases and per-head QK RMSNorm"))
+    times = _time_stack(stack, hidden, 0, None, None, bufs, 1, 3)
+    log(f"8B pp4096: {times[0]:.3f} ms/step")
+    out.append(_line(cfg, times, 3, "; q/k/v biases and per-head QK RMSNorm"))
     del stack, bufs, hidden
     torch.cuda.empty_cache()
     return out
@@ -293,18 +310,10 @@ def main():
     torch.cuda.synchronize()
     log(f"packed {cfg.n_layers} layers in {time.time() - t0:.1f}s")
 
-    stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         assert stack.run(hidden, 0, None, None, bufs) == cfg.n_layers, ddl.ddl_last_error()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        stack.run(hidden, 0, None, None, bufs)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    log(f"timed {args.steps} steps: {ms:.3f} ms/step")
+    ms, ms_med, ms_min = timed_steps(lambda: stack.run(hidden, 0, None, None, bufs), args.steps)
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step (median {ms_med:.3f}, min {ms_min:.3f})")
 
     # second pass of the same steps: HIP events around every gate/up GEMM launch
     ddl.ddl_probe_enable(ctx, ddl.DDL_K_GEMM_GATE_UP, args.steps * cfg.n_layers)
@@ -340,6 +349,7 @@ def main():
     result = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tok/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "ms_median": round(ms_med, 4), "ms_min": round(ms_min, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": "llama3b_pp512: 28 dense layers, hidden 3072, 24 q / 8 KV heads "

@@ -133,13 +133,21 @@ typedef struct {
 } ddl_layer_weights;
 
 /* 1 if the layer is one the kernels serve, 0 if not (pure host predicate;
- * the reason is in ddl_last_error()). */
+ * the reason is in ddl_last_error()).  [P1] cuda_prefill_layer answers
+ * None for a layer the launch does not serve, and [P3] LayerFfnParts::
+ * for_layer names every field so none is dropped unanswered: the same
+ * question, asked before any device memory is committed. */
 int ddl_layer_supported(const ddl_layer_desc* desc);
 
-/* Device bytes of one layer's packed weights (0 if not supported). */
+/* Device bytes of one layer's packed weights (0 if not supported): the
+ * device-resident form of the norm gains, extras and seven projections that
+ * [P1] cuda_prefill_layer borrows through each matrix's device view
+ * (`view(...)`, None when a matrix has none).  The caller allocates them. */
 size_t ddl_layer_blob_bytes(const ddl_layer_desc* desc);
 
-/* Packs a layer's weights into the caller-owned device blob `dev_blob`
+/* [P1] cuda_prefill_layer: the launch borrows each projection through a
+ * device view of its storage and the norm gains and extras as they are.
+ * Packs a layer's weights into the caller-owned device blob `dev_blob`
  * (blob_bytes >= ddl_layer_blob_bytes(desc)), on `stream`: matrices are
  * stored as fp16 holding the given values times a per-matrix power of two,
  * q/k/v stacked into one matrix and gate/up interleaved in 16-row blocks.
@@ -151,7 +159,10 @@ int ddl_layer_pack(ddl_ctx* ctx, const ddl_layer_desc* desc,
                    void* stream, ddl_layer** out);
 void ddl_layer_destroy(ddl_layer* layer);
 
-/* Workspace bytes a prefill of up to max_batch tokens at a start position of
+/* [P1] module doc: the hidden batch stays on the device between layers and
+ * every step between the seven matmuls of a layer is a kernel, so the
+ * intermediates live in device memory for the length of the call only.
+ * Workspace bytes a prefill of up to max_batch tokens at a start position of
  * up to max_start_pos needs over `n` layers (0 on bad arguments).  The
  * workspace holds the per-layer intermediates (normed rows, q/k/v, attention
  * output, SwiGLU activations) and the layer's keys and values staged as
@@ -298,7 +309,9 @@ int ddl_probe_enable(ddl_ctx* ctx, int kind, int max_launches);
  * from 0), or < 0 on error. */
 int ddl_probe_read(ddl_ctx* ctx, float* ms_out, int cap);
 
-/* The calling thread's last error or decline reason ("" if none). */
+/* The calling thread's last error or decline reason ("" if none).  [P1]
+ * warn_once prints each distinct decline message once per process; here
+ * the library only records the message and the caller de-duplicates. */
 const char* ddl_last_error(void);
 
 #ifdef __cplusplus

@@ -1,7 +1,15 @@
-"""GPU parity of ddl_attn_layer (one token against the device KV mirror)
-with the CPU oracle, and the mirror's staleness and capacity rules, through
-the C ABI.  The output hidden must match within relative L2 1e-2; the
-appended mirror row, seq_len and declines are exact."""
+"""GPU parity of ddl_attn_layer and ddl_decode_layer (one token against the
+device KV mirror) with the CPU oracle, and the mirror's staleness and
+capacity rules, through the C ABI.
+
+The single-token path computes in fp32 throughout; its weights are the
+packed fp16 matrices, which hold bf16 weights exactly.  So the output hidden
+must match the oracle within relative L2 1e-4 for bf16 weights, and 2e-3 for
+fp32 weights (rounded to fp16's 11-bit significand when packed).  At the
+decode shapes the output is mostly residual and FFN, so one case removes
+both (residual 0, down projection 0: the output is wo . attention) and holds
+the attention's own contribution to the same bound.  The appended mirror
+row, seq_len and declines are exact."""
 import sys
 import time
 
@@ -14,7 +22,12 @@ import synth
 
 pytestmark = pytest.mark.gpu
 
-TOL = 1e-2
+TOL_BF16 = 1e-4      # fp32 arithmetic, weights exact
+TOL_FP32W = 2e-3     # fp32 weights rounded to fp16 when packed
+
+
+def tol_for(cfg) -> float:
+    return TOL_BF16 if cfg.weight_dtype == "bf16" else TOL_FP32W
 
 
 def rel(a, b) -> float:
@@ -76,10 +89,14 @@ def weights_values(inp):
     return {n: synth.values(a) for n, a in inp["weights"].items()}
 
 
+@pytest.mark.timeout(300)
 @pytest.mark.parametrize("rows", synth.DECODE_ROWS)
-def test_decode_layer_matches_oracle(ddl, rows):
+def test_attn_layer_dec_sweep(ddl, rows):
+    # the decode workload: 32 q / 8 KV heads x 128, softcap 50, sigmoid gate,
+    # hidden 4096, SwiGLU 14336, at every swept context length
     cfg = synth.DECODE_CONFIG.replace(rows=rows)
-    say(f"decode rows={rows} hq={cfg.n_heads} hkv={cfg.n_kv_heads} d={cfg.d_model} f={cfg.d_ff}")
+    say(f"[attn_layer dec sweep] rows={rows} hq={cfg.n_heads} hkv={cfg.n_kv_heads} "
+        f"d={cfg.d_model} f={cfg.d_ff}")
     inp = synth.decode_inputs(cfg)
     dec = Decode(ddl, cfg, inp)
     assert dec.upload(inp["cache_k"], inp["cache_v"], rows) == 1
@@ -95,7 +112,32 @@ def test_decode_layer_matches_oracle(ddl, rows):
                              inp["cache_v"], rows, weights_values(inp), cfg, inp["residual"])
     err = rel(dec.out.cpu().numpy(), want)
     say(f"  oracle {time.time() - t0:.1f}s out rel L2 {err:.2e}")
-    assert err <= TOL
+    assert err <= TOL_BF16
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("rows", synth.DECODE_ROWS)
+def test_attn_layer_dec_attention_only(ddl, rows):
+    # residual 0 and down projection 0: out = wo . (sigmoid(gate) * attention),
+    # so the check sees the attention itself, not the residual stream
+    cfg = synth.DECODE_CONFIG.replace(rows=rows)
+    say(f"[attn_layer attention-only] rows={rows}")
+    inp = synth.decode_inputs(cfg)
+    inp["weights"] = dict(inp["weights"])
+    inp["weights"]["wd"] = np.zeros_like(inp["weights"]["wd"])
+    zero = np.zeros(cfg.d_model, np.float32)
+    dec = Decode(ddl, cfg, inp)
+    assert dec.upload(inp["cache_k"], inp["cache_v"], rows) == 1
+    assert dec.step(rows, inp["q"], inp["k"], inp["v"], inp["gate"], zero) == 1
+    w = weights_values(inp)
+    want = oracle.attn_layer(inp["q"], inp["k"], inp["v"], inp["gate"], inp["cache_k"],
+                             inp["cache_v"], rows, w, cfg, zero)
+    got = dec.out.cpu().numpy()
+    err = rel(got, want)
+    # every bit of this output comes from the attention: without it (o = 0)
+    # the output would be exactly zero
+    say(f"  out rel L2 {err:.2e}  |out| {np.linalg.norm(want):.3e}")
+    assert np.linalg.norm(want) > 0 and err <= TOL_BF16
 
 
 def small_cfg(**kw):
@@ -128,7 +170,7 @@ def test_decode_shapes(ddl, kw):
                              cfg.rows, weights_values(inp), cfg, inp["residual"])
     err = rel(dec.out.cpu().numpy(), want)
     say(f"decode {kw}: out rel L2 {err:.2e}")
-    assert err <= TOL
+    assert err <= tol_for(cfg)
 
 
 def test_decode_chain_and_mirror_rules(ddl):
@@ -148,7 +190,7 @@ def test_decode_chain_and_mirror_rules(ddl):
                             (cfg.q_width, cfg.kv_width, cfg.kv_width, cfg.q_width, cfg.d_model))
         assert dec.step(rows, q, k, v, gate, x) == 1, ddl.ddl_last_error()
         want = oracle.attn_layer(q, k, v, gate, host_k, host_v, rows, w, cfg, x)
-        assert rel(dec.out.cpu().numpy(), want) <= TOL
+        assert rel(dec.out.cpu().numpy(), want) <= TOL_BF16
         host_k, host_v = np.vstack([host_k, k]), np.vstack([host_v, v])   # the caller's push
         assert ddl.ddl_mirror_seq_len(dec.mirror) == host_k.shape[0]
     # the host cache moves backwards: the mirror is stale, declines, re-uploads
@@ -158,7 +200,7 @@ def test_decode_chain_and_mirror_rules(ddl):
     assert dec.step(30, inp["q"], inp["k"], inp["v"], inp["gate"], inp["residual"]) == 1
     want = oracle.attn_layer(inp["q"], inp["k"], inp["v"], inp["gate"], host_k, host_v, 30, w,
                              cfg, inp["residual"])
-    assert rel(dec.out.cpu().numpy(), want) <= TOL
+    assert rel(dec.out.cpu().numpy(), want) <= TOL_BF16
     # an injected failure after admission marks the mirror stale
     fctx = ddl.ddl_ctx_create(fault_after_admission=True)
     with pytest.raises(RuntimeError, match="-3"):
@@ -293,7 +335,7 @@ def test_decode_layer_matches_oracle(ddl, name):
     got_k, got_v = dl.k_row.cpu().numpy(), dl.v_row.cpu().numpy()
     err, ek, ev = rel(dl.out.cpu().numpy(), want), rel(got_k, wk), rel(got_v, wv)
     say(f"  out rel L2 {err:.2e}  k_row {ek:.2e}  v_row {ev:.2e}")
-    assert err <= TOL and ek <= 5e-3 and ev <= 5e-3
+    assert err <= tol_for(cfg) and ek <= tol_for(cfg) and ev <= tol_for(cfg)
     mk, mv = dl.mirror_row(rows)            # the appended row is the returned row, bit for bit
     np.testing.assert_array_equal(mk, got_k)
     np.testing.assert_array_equal(mv, got_v)
@@ -316,5 +358,6 @@ def test_decode_layer_chain_and_declines(ddl):
     assert torch.all(dl.out == 7.0) and ddl.ddl_mirror_seq_len(dl.mirror) == 41
     assert dl.step(41, x1) == 1
     want, wk, _ = oracle.decode_layer(x1, w, cfg, ck, cv, 41)
-    assert rel(dl.out.cpu().numpy(), want) <= TOL and rel(dl.k_row.cpu().numpy(), wk) <= 5e-3
+    assert rel(dl.out.cpu().numpy(), want) <= TOL_BF16
+    assert rel(dl.k_row.cpu().numpy(), wk) <= TOL_BF16
     assert ddl.ddl_mirror_seq_len(dl.mirror) == 42

@@ -261,11 +261,59 @@ def test_llama3b_prefix1536_full_stack(ddl):
     _full_case(ddl, "llama3b_prefix1536", synth.STACK_CONFIGS["llama3b_prefix1536"])
 
 
+@pytest.fixture(scope="module")
+def llama8b_gpu(ddl):
+    """The whole 32-layer 8B-shaped stack with biases and QK norms at pp4096,
+    run once on the GPU; the weights are drawn and packed one layer at a time."""
+    from dense_decoder_layer_amd.workloads import DeviceStack
+    cfg = synth.STACK_CONFIGS["llama8b_pp4096_extras"]
+    t0 = time.time()
+    say(f"[llama8b_pp4096_extras] packing {cfg.n_layers} layers ...")
+    ctx = ddl.ddl_ctx_create()
+    stack = DeviceStack(ctx, cfg, (synth.layer_weights(cfg, l) for l in range(cfg.n_layers)))
+    bufs = stack.buffers(cfg.batch, 0)
+    hidden = synth.hidden_rows(cfg)
+    run = stack.run(torch.from_numpy(hidden).cuda(), 0, None, None, bufs)
+    torch.cuda.synchronize()
+    out = bufs["hidden_out"].cpu().numpy()
+    ks = [t.cpu().numpy() for t in bufs["k_rows"]]
+    vs = [t.cpu().numpy() for t in bufs["v_rows"]]
+    say(f"[llama8b_pp4096_extras] GPU stack done in {time.time() - t0:.1f}s, run_len {run}")
+    del stack, bufs
+    torch.cuda.empty_cache()
+    # the oracle's hidden entering each layer, filled chunk by chunk
+    return {"cfg": cfg, "run": run, "out": out, "ks": ks, "vs": vs, "x": {0: hidden}}
+
+
+LLAMA8B_CHUNK = 8
+
+
 @pytest.mark.timeout(900)
-def test_llama8b_pp4096_extras_first_layers(ddl):
-    # the whole 32-layer stack is ~57 TFLOP of fp64 oracle work; the first
-    # two layers at the full pp4096 shape keep the check within minutes
-    _full_case(ddl, "llama8b_pp4096_extras", synth.STACK_CONFIGS["llama8b_pp4096_extras"], 2)
+@pytest.mark.parametrize("chunk", range(4))
+def test_llama8b_pp4096_extras_full_stack(llama8b_gpu, chunk):
+    # all 32 layers against the oracle, eight at a time: every layer's K/V
+    # rows, and the final hidden after the last chunk
+    st = llama8b_gpu
+    cfg = st["cfg"]
+    assert st["run"] == cfg.n_layers
+    lo = chunk * LLAMA8B_CHUNK
+    start = max(l for l in st["x"] if l <= lo)        # resume where the oracle stopped
+    x = st["x"][start]
+    for l in range(start, lo + LLAMA8B_CHUNK):
+        t0 = time.time()
+        w = {n: synth.values(a) for n, a in synth.layer_weights(cfg, l).items()}
+        x, wk, wv = oracle.dense_layer(x, w, cfg, 0)
+        st["x"][l + 1] = x
+        if l < lo:
+            continue
+        ek, ev = rel(st["ks"][l], wk), rel(st["vs"][l], wv)
+        say(f"[llama8b_pp4096_extras] layer {l}: K {ek:.2e} V {ev:.2e} "
+            f"(oracle {time.time() - t0:.1f}s)")
+        assert ek <= KV_TOL and ev <= KV_TOL
+    if lo + LLAMA8B_CHUNK == cfg.n_layers:
+        err = rel(st["out"], x)
+        say(f"[llama8b_pp4096_extras] hidden after {cfg.n_layers} layers: {err:.2e}")
+        assert np.isfinite(st["out"]).all() and err <= HIDDEN_TOL
 
 
 def test_run_of_layers_with_different_options(ddl):

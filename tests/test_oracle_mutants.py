@@ -1,5 +1,10 @@
 """Plants plausible mistakes in a temporary copy of the oracle and checks
-that the pins catch every one (CPU only; the real oracle is never edited)."""
+that the pins catch every one (CPU only; the real oracle is never edited).
+
+The committed golden sample was written by the oracle itself, so it is not
+an independent pin: the copies run every pin except that regression check,
+and an unmutated copy must pass them all (otherwise every mutant would look
+caught)."""
 import os
 import shutil
 import subprocess
@@ -57,6 +62,11 @@ MUTANTS = {
                                       "        x1 = rms_norm(x + o.reshape(B, -1) @ _f64(w[\"wo\"]).T, "
                                       "w[\"g_post_attn\"], spec.rms_eps)\n"),
     "post_ffn_norm_dropped": ("        ffn = rms_norm(ffn, w[\"g_post_ffn\"], spec.rms_eps)", "        pass"),
+    "stack_unchained": ("x, k, v = dense_layer(x, w, spec, start_pos, pk, pv)",
+                        "_, k, v = dense_layer(_f64(hidden), w, spec, start_pos, pk, pv)\n"
+                        "        x = _"),
+    "stack_rows_reversed": ("    return x, ks, vs\n", "    return x, ks[::-1], vs[::-1]\n"),
+    "stack_rows_of_first_layer": ("        ks.append(k)\n", "        ks.append(ks[0] if ks else k)\n"),
     "decode_skips_new_row": ("k_all = np.concatenate([_f64(cache_k)[:rows], _f64(k)[None]])",
                              "k_all = np.concatenate([_f64(cache_k)[:rows], "
                              "_f64(cache_k)[rows - 1:rows]])"),
@@ -69,15 +79,25 @@ def oracle_source():
         return f.read()
 
 
+def run_pins(tmp_path, source):
+    """Runs the independent pins against a copy of the oracle holding `source`."""
+    for d in ("oracle", "synth", "tests"):
+        shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
+                        ignore=shutil.ignore_patterns("__pycache__", "golden"))
+    (tmp_path / "oracle" / "__init__.py").write_text(source)
+    return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                           "-k", "not committed_sample", "tests/test_oracle_pins.py"],
+                          cwd=tmp_path, capture_output=True, text=True, timeout=300)
+
+
+def test_unmutated_copy_passes_the_pins(oracle_source, tmp_path):
+    r = run_pins(tmp_path, oracle_source)
+    assert r.returncode == 0, r.stdout[-2000:]
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_planted_mistake(name, oracle_source, tmp_path):
     before, after = MUTANTS[name]
     assert before in oracle_source, f"mutation site of {name} not found"
-    for d in ("oracle", "synth", "tests"):
-        shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
-                        ignore=shutil.ignore_patterns("__pycache__", "golden"))
-    (tmp_path / "oracle" / "__init__.py").write_text(oracle_source.replace(before, after))
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_pins.py"], cwd=tmp_path, capture_output=True,
-                       text=True, timeout=300)
+    r = run_pins(tmp_path, oracle_source.replace(before, after))
     assert r.returncode != 0, f"planted mistake {name} went unnoticed:\n{r.stdout[-2000:]}"

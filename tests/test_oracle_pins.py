@@ -436,6 +436,45 @@ def test_layer_residual_structure():
     np.testing.assert_allclose(v_rows, v.numpy(), rtol=1e-13)
 
 
+def one_token_layer_torch(x, w, spec):
+    """A layer over one new token and an empty cache, in torch library calls:
+    its only key is its own, so the attention returns v (repeated over each
+    KV head's query group), and RoPE at position 0 is the identity.
+    Returns (out, k_row, v_row)."""
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    n = lambda a, g: F.rms_norm(a, (spec.d_model,), t(g), eps=spec.rms_eps)
+    h = n(t(x), w["g_attn"])
+    k, v = h @ t(w["wk"]).T, h @ t(w["wv"]).T
+    group = spec.n_heads // spec.n_kv_heads
+    o = v.reshape(1, spec.n_kv_heads, spec.head_dim).repeat_interleave(group, dim=1).reshape(1, -1)
+    x1 = t(x) + o @ t(w["wo"]).T
+    h2 = n(x1, w["g_ffn"])
+    out = x1 + (F.silu(h2 @ t(w["wg"]).T) * (h2 @ t(w["wu"]).T)) @ t(w["wd"]).T
+    return out.numpy(), k.numpy(), v.numpy()
+
+
+def test_stack_chains_layers_and_returns_each_layers_rows():
+    # two different layers over one token: layer 1 must see layer 0's output
+    # (not the input), and the rows of layer l must be layer l's projections
+    # of its own input; both orders, plus an identity layer (wo = wd = 0)
+    spec = Spec()
+    a, b = rand_layer(spec), rand_layer(spec)
+    ident = dict(rand_layer(spec), wo=np.zeros((spec.d_model, spec.n_heads * spec.head_dim)),
+                 wd=np.zeros((spec.d_model, spec.d_ff)))
+    x = RNG.standard_normal((1, spec.d_model))
+    for first, second in ((a, b), (b, a), (ident, a), (a, ident)):
+        y, k0, v0 = one_token_layer_torch(x, first, spec)
+        z, k1, v1 = one_token_layer_torch(y, second, spec)
+        out, ks, vs = oracle.prefill_dense_stack(x, [first, second], spec, 0)
+        assert len(ks) == len(vs) == 2
+        np.testing.assert_allclose(out, z, rtol=1e-12, atol=1e-13)
+        for got, want in ((ks[0], k0), (vs[0], v0), (ks[1], k1), (vs[1], v1)):
+            np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+    # the identity layer passes its input through exactly, wherever it sits
+    out, _, _ = oracle.prefill_dense_stack(x, [ident, ident], spec, 0)
+    assert np.array_equal(out, x)
+
+
 def test_sandwich_norms_closed_form_and_scale_invariance():
     # one token, no prefix: attention returns v, so a sandwich-norm layer has
     # a closed form in library calls
