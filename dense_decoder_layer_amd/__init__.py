@@ -25,15 +25,16 @@ from ._native import (DDL_K_ATTN_PREFILL, DDL_K_DECODE_ATTN, DDL_K_DECODE_HEAD, 
                       DDL_K_RMSNORM)
 from ._native import (DDL_ACT_GELU, DDL_ACT_SWIGLU, DDL_DECLINED, DDL_DTYPE_BF16,
                       DDL_DTYPE_F32, DDL_ERR_DEVICE, DDL_ERR_INJECTED, DDL_ERR_INVALID,
-                      DDL_ERR_WORKSPACE, DDL_ROPE_NEOX, DDL_ROPE_NORM, CtxOpts, LayerDesc,
-                      LayerWeights)
+                      DDL_ERR_WORKSPACE, DDL_NOALLOC_SCRATCH_BYTES, DDL_ROPE_NEOX,
+                      DDL_ROPE_NORM, CtxOpts, LayerDesc, LayerWeights)
 
 __all__ = [
     "ddl_ctx_create", "ddl_ctx_destroy", "ddl_layer_supported", "ddl_layer_blob_bytes",
     "ddl_layer_pack", "ddl_layer_destroy", "ddl_workspace_bytes", "ddl_prefill_dense_stack",
     "ddl_mirror_bytes", "ddl_mirror_init", "ddl_mirror_upload", "ddl_mirror_seq_len",
     "ddl_mirror_capacity", "ddl_mirror_invalidate", "ddl_mirror_plan_capacity",
-    "ddl_mirror_destroy", "ddl_attn_workspace_bytes", "ddl_attn_layer", "ddl_decode_layer",
+    "ddl_mirror_destroy", "ddl_attn_workspace_bytes", "ddl_attn_layer", "ddl_attn_layer_noalloc",
+    "ddl_decode_layer",
     "ddl_last_error",
     "ddl_probe_enable", "ddl_probe_read",
     "layer_desc", "pack_layer_from_host", "Ctx", "Layer", "Mirror", "LayerDesc",
@@ -300,6 +301,21 @@ def ddl_attn_layer(ctx: Ctx, mirror: Mirror, host_rows: int, q: torch.Tensor, k:
                                workspace.numel() * workspace.element_size(), _stream(stream))
     if rc < 0:
         raise RuntimeError(f"ddl_attn_layer: {rc} {ddl_last_error()}")
+    return rc
+
+
+def ddl_attn_layer_noalloc(ctx: Ctx, mirror: Mirror, host_rows: int, q: torch.Tensor,
+                           k: torch.Tensor, v: torch.Tensor, gate: Optional[torch.Tensor],
+                           n_heads: int, softcap: float, layer: Layer, residual: torch.Tensor,
+                           out: torch.Tensor, stream=None) -> int:
+    """ddl_attn_layer with the library's fixed device scratch instead of a
+    workspace.  Returns 1 (served), 0 (declined); raises on errors (< 0)."""
+    rc = _lib().ddl_attn_layer_noalloc(ctx.handle, mirror.handle, host_rows, q.data_ptr(),
+                                       k.data_ptr(), v.data_ptr(), _ptr(gate), n_heads,
+                                       float(softcap), layer.handle, residual.data_ptr(),
+                                       out.data_ptr(), _stream(stream))
+    if rc < 0:
+        raise RuntimeError(f"ddl_attn_layer_noalloc: {rc} {ddl_last_error()}")
     return rc
 
 

@@ -15,6 +15,7 @@ DDL_ERR_WORKSPACE = -4
 DDL_ACT_SWIGLU, DDL_ACT_GELU = 0, 1
 DDL_ROPE_NEOX, DDL_ROPE_NORM = 0, 1
 DDL_DTYPE_F32, DDL_DTYPE_BF16 = 0, 1
+DDL_NOALLOC_SCRATCH_BYTES = 6 << 20
 (DDL_K_RMSNORM, DDL_K_GEMM_QKV, DDL_K_QKV_POST, DDL_K_ATTN_PREFILL, DDL_K_GEMM_WO,
  DDL_K_GEMM_GATE_UP, DDL_K_GEMM_DOWN, DDL_K_DECODE_ATTN, DDL_K_GEMV_WO, DDL_K_GEMV_GATE_UP,
  DDL_K_GEMV_DOWN, DDL_K_GEMV_QKV, DDL_K_DECODE_HEAD) = range(13)
@@ -78,6 +79,9 @@ SIGNATURES = {
     "ddl_attn_layer": (c_int, [
         c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_float,
         c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "ddl_attn_layer_noalloc": (c_int, [
+        c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_float,
+        c_void_p, c_void_p, c_void_p, c_void_p]),
     "ddl_decode_layer": (c_int, [
         c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
         c_size_t, c_void_p]),

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -739,6 +740,78 @@ int ddl_attn_layer(ddl_ctx* ctx, ddl_mirror* m, int host_rows, const float* q, c
     if (e) {
         m->seq_len = -1;
         return fail(DDL_ERR_DEVICE, std::string("attn_layer launch: ") + hipGetErrorString(e));
+    }
+    m->seq_len = host_rows + 1;
+    g_err.clear();
+    return 1;
+}
+
+}  // extern "C"
+
+// ---- ddl_attn_layer without a caller workspace -----------------------------------
+// For callers that cannot allocate device memory.  The decode scratch (split
+// partials, attention output, x1, FFN activations) lives in this file-scope
+// device array instead of a caller workspace; every call on a GPU shares that
+// GPU's copy.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in symbol): its device address is looked up once
+// per device, with that device current, and kept below.
+namespace {
+__device__ __align__(256) char scratch[DDL_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch`, or nullptr (message set).
+char* scratch_of_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        fail(DDL_ERR_DEVICE, "no current HIP device for the decode scratch");
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            fail(DDL_ERR_DEVICE, std::string("decode scratch address: ") + hipGetErrorString(e));
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = static_cast<char*>(p);
+    }
+    return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int ddl_attn_layer_noalloc(ddl_ctx* ctx, ddl_mirror* m, int host_rows, const float* q,
+                           const float* k, const float* v, const float* gate, int n_heads,
+                           float softcap, const ddl_layer* L, const float* residual, float* out,
+                           void* stream) {
+    if (!ctx || !m || !q || !k || !v || !L || !residual || !out)
+        return fail(DDL_ERR_INVALID, "null argument");
+    if (decode_refused(m, host_rows, n_heads, L)) return DDL_DECLINED;
+    if (!(softcap >= 0.0f)) return fail(DDL_ERR_INVALID, "negative softcap");
+    const AttnWs W = attn_ws(L);
+    if (W.total > DDL_NOALLOC_SCRATCH_BYTES)
+        return fail(DDL_ERR_WORKSPACE,
+                    "layer needs " + std::to_string(W.total) +
+                        " bytes of decode scratch, above the fixed DDL_NOALLOC_SCRATCH_BYTES (" +
+                        std::to_string((size_t)DDL_NOALLOC_SCRATCH_BYTES) +
+                        "); use ddl_attn_layer with a workspace");
+    char* ws = scratch_of_current_device();
+    if (!ws) return DDL_ERR_DEVICE;
+    if (ctx->fault_after_admission) {
+        m->seq_len = -1;
+        return fail(DDL_ERR_INJECTED, "injected fault after admission");
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = attn_and_tail(ctx, m, host_rows, q, k, v, gate, softcap, L, residual, out,
+                                       ws, W, s);
+    if (e) {
+        m->seq_len = -1;
+        return fail(DDL_ERR_DEVICE, std::string("attn_layer_noalloc launch: ") + hipGetErrorString(e));
     }
     m->seq_len = host_rows + 1;
     g_err.clear();

@@ -255,6 +255,25 @@ int ddl_attn_layer(ddl_ctx* ctx, ddl_mirror* mirror, int host_rows,
                    const ddl_layer* layer, const float* residual, float* out,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* ddl_attn_layer for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same refusals, kernels and results, with no workspace argument.  The
+ * decode scratch is a fixed device array of DDL_NOALLOC_SCRATCH_BYTES
+ * inside the library, one copy per GPU, held until the process ends; the
+ * call allocates nothing (no hipMalloc, hipFree or allocating library call).
+ * A layer whose scratch (ddl_attn_workspace_bytes) exceeds that size
+ * returns DDL_ERR_WORKSPACE with nothing enqueued -- 32 query heads of 128
+ * with hidden 4096 and FFN 14336 need about 4.3 MB.  Every call on one GPU
+ * uses the same array: calls that overlap on one GPU (other streams, other
+ * threads, other contexts) race and give undefined results; calls ordered
+ * on one stream are fine.  Returns as ddl_attn_layer. */
+#define DDL_NOALLOC_SCRATCH_BYTES (6u << 20)
+int ddl_attn_layer_noalloc(ddl_ctx* ctx, ddl_mirror* mirror, int host_rows,
+                           const float* q, const float* k, const float* v,
+                           const float* gate, int n_heads, float softcap,
+                           const ddl_layer* layer, const float* residual,
+                           float* out, void* stream);
+
 /* One token's whole decoder layer against the mirror, every step on the
  * device: the head ([P1] cuda_prefill_layer's attention norm, stacked
  * q/k/v(/gate) projection, extras and RoPE description) feeding the
