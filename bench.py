@@ -107,7 +107,7 @@ def decode_bench(ddl, ctx, reps=40):
     cfg = synth.DECODE_CONFIG
     inp = synth.decode_inputs(cfg)
     layer = ddl.pack_layer_from_host(ctx, desc_for(cfg.stack_view()), inp["weights"])
-    cap = ddl.ddl_mirror_plan_capacity(cfg.rows, cfg.rows + 9 * reps + 16)   # every call appends a row
+    cap = ddl.ddl_mirror_plan_capacity(cfg.rows, cfg.rows + 14 * reps + 32)   # every call appends a row
     mirrors, bufs = [], []
     k = torch.from_numpy(inp["cache_k"]).cuda()
     v = torch.from_numpy(inp["cache_v"]).cuda()
@@ -188,12 +188,42 @@ def decode_bench(ddl, ctx, reps=40):
         d = ddl.ddl_probe_read(ctx, reps)
         ddl.ddl_probe_enable(ctx, kind, 0)
         tail[name + "_us"] = round(sum(d) / len(d) * 1e3, 2)
+    # the same step captured once per mirror as a HIP graph and replayed
+    graphs = [ddl.ddl_decode_graph_create(ctx, m, layer, hid, out, k_row, v_row, w)
+              for m, w in zip(mirrors, (ws, torch.empty_like(ws)))]
+
+    def gcall(i):
+        m = mirrors[i % 2]
+        rc = ddl.ddl_decode_graph_launch(ctx, graphs[i % 2], ddl.ddl_mirror_seq_len(m))
+        assert rc == 1, ddl.ddl_last_error()
+
+    for i in range(4):
+        gcall(i)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(reps):
+        gcall(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = start.elapsed_time(end) / reps
+    # one token at a time, the host waiting for each (a decode loop that
+    # samples between tokens): the submissions of a step are on the path
+    sync = {}
+    for name, fn in (("decode_layer_sync_ms", dcall), ("decode_graph_sync_ms", gcall)):
+        t0 = time.perf_counter()
+        for i in range(reps):
+            fn(i)
+            torch.cuda.synchronize()
+        sync[name] = round((time.perf_counter() - t0) / reps * 1e3, 4)
+    del graphs
     attn_bytes = attended * cfg.kv_width * 4 * 2 // reps     # fp32 K and V rows read per call
     return {"config": f"{cfg.name}: {cfg.rows} cached rows, {cfg.n_heads} q / {cfg.n_kv_heads} "
                       f"KV heads x {cfg.head_dim}, softcap {cfg.softcap:g}, sigmoid gate, "
                       f"wo + RMSNorm + SwiGLU {cfg.d_ff} tail, hidden {cfg.d_model}",
             "ms_per_layer": round(layer_ms, 4),
             "decode_layer_ms": round(full_ms, 4),   # ddl_decode_layer: head on the device too
+            "decode_graph_ms": round(graph_ms, 4),  # the same step replayed as one HIP graph
+            **sync,
             "attn_us": round(attn_ms * 1e3, 2),
             "attn_bytes": attn_bytes,
             "attn_hbm_gbs": round(attn_bytes / (attn_ms / 1e3) / 1e9, 1),
@@ -240,7 +270,7 @@ def _line(cfg, times, steps, note):
             "mfma_peak_frac": round(flops / (ms / 1e3) / 1e12 / PEAK_MFMA_TFLOPS, 4)}
 
 
-def secondary_bench(ddl, ctx, stack3b, hidden3b, args):
+def secondary_bench(ddl, ctx, stack3b, hidden3b, args, which=("prefix1536", "pp4096")):
     """The other prefill workloads, each a whole stack per step with inputs
     resident in HBM: the 3B stack over a 1536-row cached prefix per layer
     (the same seeded weights as the headline, so the packed stack is reused),
@@ -249,30 +279,50 @@ def secondary_bench(ddl, ctx, stack3b, hidden3b, args):
     import synth
     from dense_decoder_layer_amd.workloads import DeviceStack
     out = []
-    cfg = synth.STACK_CONFIGS["llama3b_prefix1536"]
-    pk, pv = [], []
-    for l in range(cfg.n_layers):
-        k, v = synth.prefix_rows(cfg, l)
-        pk.append(torch.from_numpy(k).cuda())
-        pv.append(torch.from_numpy(v).cuda())
-    bufs = stack3b.buffers(cfg.batch, cfg.start_pos)
-    steps = max(3, min(args.steps, 10))
-    times = _time_stack(stack3b, hidden3b, cfg.start_pos, pk, pv, bufs, 2, steps)
-    log(f"3B over a 1536-row prefix: {times[0]:.3f} ms/step")
-    out.append(_line(cfg, times, steps, "; prefix K/V rows fp32 resident per layer"))
-    del pk, pv, bufs
-    cfg = synth.STACK_CONFIGS["llama8b_pp4096_extras"]
-    t0 = time.time()
-    stack = DeviceStack(ctx, cfg, (synth.layer_weights(cfg, l) for l in range(cfg.n_layers)))
-    hidden = torch.from_numpy(synth.hidden_rows(cfg)).cuda()
-    bufs = stack.buffers(cfg.batch, 0)
-    log(f"packed the 8B stack in {time.time() - t0:.1f}s")
-    times = _time_stack(stack, hidden, 0, None, None, bufs, 1, 3)
-    log(f"8B pp4096: {times[0]:.3f} ms/step")
-    out.append(_line(cfg, times, 3, "; q/k/v biases and per-head QK RMSNorm"))
-    del stack, bufs, hidden
+    if "prefix1536" in which:
+        cfg = synth.STACK_CONFIGS["llama3b_prefix1536"]
+        pk, pv = [], []
+        for l in range(cfg.n_layers):
+            k, v = synth.prefix_rows(cfg, l)
+            pk.append(torch.from_numpy(k).cuda())
+            pv.append(torch.from_numpy(v).cuda())
+        bufs = stack3b.buffers(cfg.batch, cfg.start_pos)
+        steps = max(3, min(args.steps, 10))
+        times = _time_stack(stack3b, hidden3b, cfg.start_pos, pk, pv, bufs, 2, steps)
+        log(f"3B over a 1536-row prefix: {times[0]:.3f} ms/step")
+        out.append(_line(cfg, times, steps, "; prefix K/V rows fp32 resident per layer"))
+        del pk, pv, bufs
+    if "pp4096" in which:
+        cfg = synth.STACK_CONFIGS["llama8b_pp4096_extras"]
+        t0 = time.time()
+        stack = DeviceStack(ctx, cfg, (synth.layer_weights(cfg, l) for l in range(cfg.n_layers)))
+        hidden = torch.from_numpy(synth.hidden_rows(cfg)).cuda()
+        bufs = stack.buffers(cfg.batch, 0)
+        log(f"packed the 8B stack in {time.time() - t0:.1f}s")
+        times = _time_stack(stack, hidden, 0, None, None, bufs, 1, 3)
+        log(f"8B pp4096: {times[0]:.3f} ms/step")
+        out.append(_line(cfg, times, 3, "; q/k/v biases and per-head QK RMSNorm"))
+        del stack, bufs, hidden
     torch.cuda.empty_cache()
     return out
+
+
+def secondary_only(which, args):
+    """One secondary workload alone (for a per-workload profile): prints its
+    line, not the headline's."""
+    import torch
+    import dense_decoder_layer_amd as ddl
+    import synth
+    from dense_decoder_layer_amd.workloads import DeviceStack
+    torch.cuda.set_device(0)
+    ctx = ddl.ddl_ctx_create()
+    stack = hidden = None
+    if which == "prefix1536":
+        cfg = synth.STACK_CONFIGS["llama3b_pp512"]
+        stack = DeviceStack(ctx, cfg, (synth.layer_weights(cfg, l) for l in range(cfg.n_layers)))
+        hidden = torch.from_numpy(synth.hidden_rows(cfg)).cuda()
+    print(json.dumps({"secondary": secondary_bench(ddl, ctx, stack, hidden, args, (which,))}),
+          flush=True)
 
 
 def main():
@@ -285,6 +335,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the other prefill workloads (3B over a 1536-row prefix, 8B pp4096)")
+    ap.add_argument("--secondary-only", choices=("prefix1536", "pp4096"),
+                    help="time one secondary workload alone (profiling aid; no headline line)")
     ap.add_argument("--breakdown", action="store_true",
                     help="also time every prefill kernel class per launch (HIP events)")
     args = ap.parse_args()
@@ -293,6 +345,10 @@ def main():
                                    "is a design (DESIGN.md), not a launched path",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+
+    if args.secondary_only:
+        secondary_only(args.secondary_only, args)
+        return
 
     import torch
     import dense_decoder_layer_amd as ddl

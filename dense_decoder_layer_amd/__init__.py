@@ -34,7 +34,8 @@ __all__ = [
     "ddl_mirror_bytes", "ddl_mirror_init", "ddl_mirror_upload", "ddl_mirror_seq_len",
     "ddl_mirror_capacity", "ddl_mirror_invalidate", "ddl_mirror_plan_capacity",
     "ddl_mirror_destroy", "ddl_attn_workspace_bytes", "ddl_attn_layer", "ddl_attn_layer_noalloc",
-    "ddl_decode_layer",
+    "ddl_decode_layer", "ddl_decode_graph_create", "ddl_decode_graph_launch",
+    "ddl_decode_graph_destroy", "DecodeGraph",
     "ddl_last_error",
     "ddl_probe_enable", "ddl_probe_read",
     "layer_desc", "pack_layer_from_host", "Ctx", "Layer", "Mirror", "LayerDesc",
@@ -330,3 +331,46 @@ def ddl_decode_layer(ctx: Ctx, mirror: Mirror, host_rows: int, hidden: torch.Ten
     if rc < 0:
         raise RuntimeError(f"ddl_decode_layer: {rc} {ddl_last_error()}")
     return rc
+
+
+class DecodeGraph:
+    """A captured decode step; keeps the buffers it is bound to alive."""
+
+    def __init__(self, handle: int, keep):
+        self.handle, self._keep = handle, keep
+
+    def __del__(self):
+        if getattr(self, "handle", None) and ddl_decode_graph_destroy is not None:
+            ddl_decode_graph_destroy(self)
+
+
+def ddl_decode_graph_create(ctx: Ctx, mirror: Mirror, layer: Layer, hidden: torch.Tensor,
+                            out: torch.Tensor, k_row: torch.Tensor, v_row: torch.Tensor,
+                            workspace: torch.Tensor) -> Optional[DecodeGraph]:
+    """Captures one ddl_decode_layer step bound to these buffers; None when
+    declined; raises on errors."""
+    g = c_void_p()
+    rc = _lib().ddl_decode_graph_create(ctx.handle, mirror.handle, layer.handle,
+                                        hidden.data_ptr(), out.data_ptr(), k_row.data_ptr(),
+                                        v_row.data_ptr(), workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(), byref(g))
+    if rc < 0:
+        raise RuntimeError(f"ddl_decode_graph_create: {rc} {ddl_last_error()}")
+    if rc == 0:
+        return None
+    return DecodeGraph(g.value, (ctx, mirror, layer, hidden, out, k_row, v_row, workspace))
+
+
+def ddl_decode_graph_launch(ctx: Ctx, graph: DecodeGraph, host_rows: int, stream=None) -> int:
+    """Returns 1 (served), 0 (declined); raises on errors (< 0)."""
+    rc = _lib().ddl_decode_graph_launch(ctx.handle, graph.handle, host_rows, _stream(stream))
+    if rc < 0:
+        raise RuntimeError(f"ddl_decode_graph_launch: {rc} {ddl_last_error()}")
+    return rc
+
+
+def ddl_decode_graph_destroy(graph: DecodeGraph) -> None:
+    if graph.handle:
+        _lib().ddl_decode_graph_destroy(graph.handle)
+        graph.handle = None
+

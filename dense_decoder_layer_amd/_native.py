@@ -85,6 +85,11 @@ SIGNATURES = {
     "ddl_decode_layer": (c_int, [
         c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
         c_size_t, c_void_p]),
+    "ddl_decode_graph_create": (c_int, [
+        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+        POINTER(c_void_p)]),
+    "ddl_decode_graph_launch": (c_int, [c_void_p, c_void_p, c_int, c_void_p]),
+    "ddl_decode_graph_destroy": (None, [c_void_p]),
     "ddl_probe_enable": (c_int, [c_void_p, c_int, c_int]),
     "ddl_probe_read": (c_int, [c_void_p, POINTER(c_float), c_int]),
     "ddl_last_error": (c_char_p, []),

@@ -424,8 +424,8 @@ int ddl_prefill_dense_stack(ddl_ctx* ctx, const float* hidden, const ddl_layer* 
     const int d = L0->d, hq = L0->hq, hkv = L0->hkv, hd = L0->hd, f = L0->f, nqkv = L0->nqkv;
     // K splits of the projections (gate/up never splits); a split GEMM's
     // partial sums are added by the kernel that consumes its output: the QKV
-    // post-step, the FFN norm, the next layer's attention norm.  The run's
-    // last down projection does not split, so hidden_out is complete.
+    // post-step, the FFN norm, the next layer's attention norm, and after
+    // the run's last down projection a closing row kernel.
     const int sp_qkv = gemm_splits(batch, nqkv, d, EPI_F32);
     const int sp_wo = gemm_splits(batch, d, hq * hd, EPI_RESID);
     const int sp_down = gemm_splits(batch, d, f, EPI_RESID);
@@ -524,16 +524,14 @@ int ddl_prefill_dense_stack(ddl_ctx* ctx, const float* hidden, const ddl_layer* 
             g.M = batch; g.N = d; g.K = f;
             g.inv_scale = &L->hdr->inv_scale[MAT_D];
             g.C = hidden_out; g.ldc = d; g.R = L->g_post_ffn ? nullptr : x1; g.ldr = d; g.P = part;
-            // the run's last down projection splits only when a norm kernel
-            // follows it anyway (a post-FFN norm)
-            const int sp = l + 1 < run || L->g_post_ffn ? sp_down : 1;
             ProbeScope p(ctx, DDL_K_GEMM_DOWN, s);
-            e = launch_gemm(g, EPI_RESID, sp, s);
-            pending = sp - 1;
+            e = launch_gemm(g, EPI_RESID, sp_down, s);
+            pending = sp_down - 1;
             pending_gpost = L->g_post_ffn;
         }
     }
-    if (!e && pending_gpost) {   // the last layer's post-FFN norm and residual
+    if (!e && (pending > 0 || pending_gpost)) {
+        // the last down projection's partials, and a post-FFN norm's residual
         ProbeScope p(ctx, DDL_K_RMSNORM, s);
         e = launch_rmsnorm_f16(hidden_out, nullptr, nullptr, batch, d, layers[run - 1]->eps, part,
                                pending, x1, pending_gpost, s);
@@ -610,7 +608,7 @@ int ddl_mirror_plan_capacity(int rows, int planned) {
 
 namespace {
 struct AttnWs {
-    size_t pm, pl, po, o, x1, a, qkv, q, total;
+    size_t pm, pl, po, o, x1, a, qkv, q, rdev, total;
 };
 // Partials are sized for the largest split count, so one workspace serves
 // every row count.
@@ -631,6 +629,7 @@ AttnWs attn_ws(const ddl_layer* L) {
     w.a = take((size_t)L->f * 4);
     w.qkv = take((size_t)L->nqkv * 4);      // ddl_decode_layer's head
     w.q = take((size_t)L->hq * L->hd * 4);
+    w.rdev = take(sizeof(int));             // a decode graph's device row count
     w.total = o;
     return w;
 }
@@ -640,15 +639,24 @@ AttnWs attn_ws(const ddl_layer* L) {
 // trusted only while it holds exactly the cache's rows and needs room for
 // one more; device_attention_shape_ok: no sliding window).  True when the
 // call is declined (the reason is in the last error).
-bool decode_refused(const ddl_mirror* m, int host_rows, int n_heads, const ddl_layer* L) {
+bool decode_rows_refused(const ddl_mirror* m, int host_rows) {
+    if (m->seq_len != host_rows) {
+        fail(DDL_DECLINED, "mirror is stale (seq_len differs from the cache's rows)");
+        return true;
+    }
+    if (host_rows < 0 || m->cap < host_rows + 1) {
+        fail(DDL_DECLINED, "mirror capacity below rows + 1");
+        return true;
+    }
+    return false;
+}
+
+// The shape half of the refusals (the same for every row count).
+bool decode_shape_refused(const ddl_mirror* m, int n_heads, const ddl_layer* L) {
     auto no = [](const char* why) {
         fail(DDL_DECLINED, why);
         return true;
     };
-    if (m->seq_len != host_rows)
-        return no("mirror is stale (seq_len differs from the cache's rows)");
-    if (host_rows < 0 || m->cap < host_rows + 1)
-        return no("mirror capacity below rows + 1");
     if (n_heads != L->hq || m->hkv != L->hkv || m->hd != L->hd)
         return no("head shape differs between call, layer and mirror");
     if (!decode_group_ok(L->hq, L->hkv, L->hd))
@@ -662,12 +670,18 @@ bool decode_refused(const ddl_mirror* m, int host_rows, int n_heads, const ddl_l
     return false;
 }
 
+bool decode_refused(const ddl_mirror* m, int host_rows, int n_heads, const ddl_layer* L) {
+    return decode_rows_refused(m, host_rows) || decode_shape_refused(m, n_heads, L);
+}
+
 // Attention against the mirror (appending row host_rows) and the tail:
 // x1 = x + wo . o; out = x1 + down(act(gate(h2)) * up(h2)), h2 = rms_norm(x1).
+// With rdev the row count is read from device memory (a captured step) and
+// the split plan is the one for the mirror's full capacity.
 hipError_t attn_and_tail(ddl_ctx* ctx, ddl_mirror* m, int host_rows, const float* q,
                          const float* k, const float* v, const float* gate, float softcap,
                          const ddl_layer* L, const float* residual, float* out, char* ws,
-                         const AttnWs& W, hipStream_t s) {
+                         const AttnWs& W, hipStream_t s, int* rdev = nullptr) {
     float* o = reinterpret_cast<float*>(ws + W.o);
     float* x1 = reinterpret_cast<float*>(ws + W.x1);
     float* a = reinterpret_cast<float*>(ws + W.a);
@@ -678,7 +692,9 @@ hipError_t attn_and_tail(ddl_ctx* ctx, ddl_mirror* m, int host_rows, const float
     d.part_o = reinterpret_cast<float*>(ws + W.po);
     d.o = o;
     d.R = host_rows; d.hq = L->hq; d.hkv = L->hkv; d.hd = L->hd;
-    decode_split_plan(L->hq, L->hkv, L->hd, host_rows + 1, &d.n_splits, &d.rows_per_split);
+    d.R_dev = rdev;
+    decode_split_plan(L->hq, L->hkv, L->hd, rdev ? m->cap : host_rows + 1, &d.n_splits,
+                      &d.rows_per_split);
     d.softcap = softcap;
     hipError_t e;
     {
@@ -818,22 +834,14 @@ int ddl_attn_layer_noalloc(ddl_ctx* ctx, ddl_mirror* m, int host_rows, const flo
     return 1;
 }
 
-int ddl_decode_layer(ddl_ctx* ctx, ddl_mirror* m, int host_rows, const float* hidden,
-                     const ddl_layer* L, float* out, float* k_row, float* v_row,
-                     void* workspace, size_t workspace_bytes, void* stream) {
-    if (!ctx || !m || !hidden || !L || !out || !k_row || !v_row)
-        return fail(DDL_ERR_INVALID, "null argument");
-    if (decode_refused(m, host_rows, L->hq, L)) return DDL_DECLINED;
-    if (!gemv_shape_ok(L->d) || L->nqkv % 32) return fail(DDL_DECLINED, "GEMV width not served");
-    const AttnWs W = attn_ws(L);
-    if (!workspace || workspace_bytes < W.total)
-        return fail(DDL_ERR_WORKSPACE, "workspace smaller than ddl_attn_workspace_bytes");
-    if (ctx->fault_after_admission) {
-        m->seq_len = -1;
-        return fail(DDL_ERR_INJECTED, "injected fault after admission");
-    }
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    char* ws = static_cast<char*>(workspace);
+}  // extern "C"
+
+namespace {
+// One whole decode step (head, attention, tail) on s; with rdev the row
+// count and the position are read from device memory.
+hipError_t decode_step(ddl_ctx* ctx, ddl_mirror* m, int host_rows, const float* hidden,
+                       const ddl_layer* L, float* out, float* k_row, float* v_row, char* ws,
+                       const AttnWs& W, hipStream_t s, int* rdev) {
     float* qkv = reinterpret_cast<float*>(ws + W.qkv);
     float* q = reinterpret_cast<float*>(ws + W.q);
     hipError_t e;
@@ -850,7 +858,7 @@ int ddl_decode_layer(ddl_ctx* ctx, ddl_mirror* m, int host_rows, const float* hi
         h.qkv = qkv; h.bias = L->bqkv; h.q_norm = L->q_norm; h.k_norm = L->k_norm; h.eps = L->eps;
         h.rope_on = L->rope_on; h.rope_layout = L->rope_layout; h.rot_dim = L->rot_dim;
         h.theta = L->theta; h.freq = L->freq; h.mscale = L->mscale;
-        h.pos = host_rows; h.hq = L->hq; h.hkv = L->hkv; h.hd = L->hd;
+        h.pos = host_rows; h.pos_dev = rdev; h.hq = L->hq; h.hkv = L->hkv; h.hd = L->hd;
         h.q = q; h.k_row = k_row; h.v_row = v_row;
         ProbeScope p(ctx, DDL_K_DECODE_HEAD, s);
         e = launch_decode_head(h, s);
@@ -858,8 +866,31 @@ int ddl_decode_layer(ddl_ctx* ctx, ddl_mirror* m, int host_rows, const float* hi
     if (!e) {
         const float* gate = L->gated ? qkv + (size_t)(L->hq + 2 * L->hkv) * L->hd : nullptr;
         e = attn_and_tail(ctx, m, host_rows, q, k_row, v_row, gate, L->softcap, L, hidden, out, ws,
-                          W, s);
+                          W, s, rdev);
     }
+    return e;
+}
+}  // namespace
+
+extern "C" {
+
+int ddl_decode_layer(ddl_ctx* ctx, ddl_mirror* m, int host_rows, const float* hidden,
+                     const ddl_layer* L, float* out, float* k_row, float* v_row,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    if (!ctx || !m || !hidden || !L || !out || !k_row || !v_row)
+        return fail(DDL_ERR_INVALID, "null argument");
+    if (decode_refused(m, host_rows, L->hq, L)) return DDL_DECLINED;
+    if (!gemv_shape_ok(L->d) || L->nqkv % 32) return fail(DDL_DECLINED, "GEMV width not served");
+    const AttnWs W = attn_ws(L);
+    if (!workspace || workspace_bytes < W.total)
+        return fail(DDL_ERR_WORKSPACE, "workspace smaller than ddl_attn_workspace_bytes");
+    if (ctx->fault_after_admission) {
+        m->seq_len = -1;
+        return fail(DDL_ERR_INJECTED, "injected fault after admission");
+    }
+    const hipError_t e = decode_step(ctx, m, host_rows, hidden, L, out, k_row, v_row,
+                                     static_cast<char*>(workspace), W,
+                                     static_cast<hipStream_t>(stream), nullptr);
     if (e) {
         m->seq_len = -1;
         return fail(DDL_ERR_DEVICE, std::string("decode_layer launch: ") + hipGetErrorString(e));
@@ -867,6 +898,99 @@ int ddl_decode_layer(ddl_ctx* ctx, ddl_mirror* m, int host_rows, const float* hi
     m->seq_len = host_rows + 1;
     g_err.clear();
     return 1;
+}
+
+}  // extern "C"
+
+// ---- a decode step captured once and replayed per token -----------------------
+struct ddl_decode_graph {
+    ddl_mirror* m;
+    const ddl_layer* L;
+    hipStream_t capture;     // the stream the step was captured on
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+    int* rdev;               // device row count, in the caller's workspace
+    int shadow;              // the count rdev holds once enqueued work is done; -1 unknown
+};
+
+namespace {
+void graph_release(ddl_decode_graph* g) {
+    if (g->exec) hipGraphExecDestroy(g->exec);
+    if (g->graph) hipGraphDestroy(g->graph);
+    if (g->capture) hipStreamDestroy(g->capture);
+    delete g;
+}
+}  // namespace
+
+extern "C" {
+
+int ddl_decode_graph_create(ddl_ctx* ctx, ddl_mirror* m, const ddl_layer* L,
+                            const float* hidden, float* out, float* k_row, float* v_row,
+                            void* workspace, size_t workspace_bytes, ddl_decode_graph** out_graph) {
+    if (!ctx || !m || !L || !hidden || !out || !k_row || !v_row || !out_graph)
+        return fail(DDL_ERR_INVALID, "null argument");
+    if (decode_shape_refused(m, L->hq, L)) return DDL_DECLINED;
+    if (!gemv_shape_ok(L->d) || L->nqkv % 32) return fail(DDL_DECLINED, "GEMV width not served");
+    const AttnWs W = attn_ws(L);
+    if (!workspace || workspace_bytes < W.total)
+        return fail(DDL_ERR_WORKSPACE, "workspace smaller than ddl_attn_workspace_bytes");
+    ddl_decode_graph* g = new (std::nothrow) ddl_decode_graph{};
+    if (!g) return fail(DDL_ERR_INVALID, "out of host memory");
+    g->m = m;
+    g->L = L;
+    char* ws = static_cast<char*>(workspace);
+    g->rdev = reinterpret_cast<int*>(ws + W.rdev);
+    g->shadow = -1;
+    // capture on a stream of the library's own (the caller's may be the
+    // null stream, which cannot be captured), with the launch probes off
+    hipError_t e = hipStreamCreateWithFlags(&g->capture, hipStreamNonBlocking);
+    if (!e) e = hipStreamBeginCapture(g->capture, hipStreamCaptureModeRelaxed);
+    if (!e) {
+        const int kind = ctx->probe_kind;
+        ctx->probe_kind = -1;
+        const hipError_t le = decode_step(ctx, m, 0, hidden, L, out, k_row, v_row, ws, W,
+                                          g->capture, g->rdev);
+        ctx->probe_kind = kind;
+        e = hipStreamEndCapture(g->capture, &g->graph);
+        if (!e) e = le;
+    }
+    if (!e) e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
+    if (e) {
+        graph_release(g);
+        return fail(DDL_ERR_DEVICE, std::string("decode graph capture: ") + hipGetErrorString(e));
+    }
+    *out_graph = g;
+    g_err.clear();
+    return 1;
+}
+
+int ddl_decode_graph_launch(ddl_ctx* ctx, ddl_decode_graph* g, int host_rows, void* stream) {
+    if (!ctx || !g) return fail(DDL_ERR_INVALID, "null argument");
+    ddl_mirror* m = g->m;
+    if (decode_rows_refused(m, host_rows)) return DDL_DECLINED;
+    if (ctx->fault_after_admission) {
+        m->seq_len = -1;
+        return fail(DDL_ERR_INJECTED, "injected fault after admission");
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    // the device count follows the graph's own replays; anything else that
+    // moved the mirror (an upload, an eager step) is caught up first
+    if (g->shadow != host_rows) e = launch_set_int(g->rdev, host_rows, s);
+    if (!e) e = hipGraphLaunch(g->exec, s);
+    if (e) {
+        m->seq_len = -1;
+        g->shadow = -1;
+        return fail(DDL_ERR_DEVICE, std::string("decode graph launch: ") + hipGetErrorString(e));
+    }
+    g->shadow = host_rows + 1;
+    m->seq_len = host_rows + 1;
+    g_err.clear();
+    return 1;
+}
+
+void ddl_decode_graph_destroy(ddl_decode_graph* g) {
+    if (g) graph_release(g);
 }
 
 }  // extern "C"

@@ -41,7 +41,8 @@ __global__ __launch_bounds__(ROWS_WAVES * 64) void decode_attn_rows_kernel(Decod
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane / LPH, sub = lane % LPH;
     const int kvw = HKV * HD;
-    const int nrows = p.R + 1;
+    const int R = p.R_dev ? *p.R_dev : p.R;
+    const int nrows = R + 1;
     const int split = blockIdx.x, ns = p.n_splits;
     const float LOG2E = 1.4426950408889634f;
     // chunk c of the lane: dims c*4*LPH + sub*4 .. +3 of KV head g; q is
@@ -66,8 +67,8 @@ __global__ __launch_bounds__(ROWS_WAVES * 64) void decode_attn_rows_kernel(Decod
     }
     const float cap = p.softcap, inv_cap = cap > 0.f ? 1.0f / cap : 0.f;
     for (int r = split + ns * wave; r < nrows; r += ns * NW) {
-        const float* ks = r < p.R ? p.mk + (size_t)r * kvw : p.knew;
-        const float* vs = r < p.R ? p.mv + (size_t)r * kvw : p.vnew;
+        const float* ks = r < R ? p.mk + (size_t)r * kvw : p.knew;
+        const float* vs = r < R ? p.mv + (size_t)r * kvw : p.vnew;
         float kx[DPL], vx[DPL];
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(ROWS_WAVES * 64) void decode_attn_rows_kernel(Decod
             kx[4 * c] = kk.x; kx[4 * c + 1] = kk.y; kx[4 * c + 2] = kk.z; kx[4 * c + 3] = kk.w;
             vx[4 * c] = vv.x; vx[4 * c + 1] = vv.y; vx[4 * c + 2] = vv.z; vx[4 * c + 3] = vv.w;
         }
-        if (r == p.R) {   // append this token's row to the mirror
+        if (r == R) {   // append this token's row to the mirror
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 const size_t at = (size_t)r * kvw + g * HD + c * 4 * LPH + sub * 4;
@@ -171,9 +172,13 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(DecodeAttnArgs p
     const int grp = lane >> 4, sub = lane & 15;
     const int split = blockIdx.x, g = blockIdx.y;
     const int kvw = p.hkv * HD;
-    const int nrows = p.R + 1;
-    const int r0 = split * p.rows_per_split;
-    const int r1 = min(r0 + p.rows_per_split, nrows);
+    const int R = p.R_dev ? *p.R_dev : p.R;
+    const int nrows = R + 1;
+    // with the count in device memory the split count is fixed (by the
+    // mirror's capacity) and the rows are dealt out here, 16 at a time
+    const int per = p.R_dev ? (((nrows + p.n_splits - 1) / p.n_splits + 15) / 16) * 16 : p.rows_per_split;
+    const int r0 = split * per;
+    const int r1 = min(r0 + per, nrows);
     const float LOG2E = 1.4426950408889634f;
     const float scale = 1.0f / sqrtf((float)HD);
 
@@ -204,8 +209,8 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(DecodeAttnArgs p
         for (int u = 0; u < U; ++u) {
             const int r = base + u * 16 + wave * 4 + grp;
             valid[u] = r < r1;
-            const float* ksrc = r < p.R ? p.mk + (size_t)r * kvw + g * HD : p.knew + g * HD;
-            const float* vsrc = r < p.R ? p.mv + (size_t)r * kvw + g * HD : p.vnew + g * HD;
+            const float* ksrc = r < R ? p.mk + (size_t)r * kvw + g * HD : p.knew + g * HD;
+            const float* vsrc = r < R ? p.mv + (size_t)r * kvw + g * HD : p.vnew + g * HD;
 #pragma unroll
             for (int j = 0; j < NF4; ++j) {
                 float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
@@ -220,7 +225,7 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(DecodeAttnArgs p
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int r = base + u * 16 + wave * 4 + grp;
-            if (valid[u] && r == p.R) {   // append this token's row to the mirror
+            if (valid[u] && r == R) {   // append this token's row to the mirror
 #pragma unroll
                 for (int j = 0; j < NF4; ++j) {
                     const size_t at = (size_t)r * kvw + g * HD + j * 64 + sub * 4;
@@ -363,6 +368,9 @@ __global__ __launch_bounds__(COMBINE_GROUPS * 32) void decode_attn_combine_kerne
         float r = T / L;
         if (p.gate) r *= 1.0f / (1.0f + expf(-p.gate[(size_t)h * HD + d0 + tid]));
         p.o[(size_t)h * HD + d0 + tid] = r;
+        // a replayed step: the head and the attention kernels, which read
+        // the count, have finished (stream order), so it advances here
+        if (p.R_dev && h == 0 && blockIdx.y == 0 && tid == 0) p.R_dev[0] = p.R_dev[0] + 1;
     }
 }
 
@@ -618,7 +626,7 @@ __global__ __launch_bounds__(HD) void decode_head_kernel(DecodeHeadArgs p) {
                 }
                 double inv = pow(p.theta, -2.0 * (double)i / (double)rd);
                 if (p.freq) inv /= (double)p.freq[i];
-                const double ang = (double)p.pos * inv;
+                const double ang = (double)(p.pos_dev ? *p.pos_dev : p.pos) * inv;
                 const float c = (float)(p.mscale * cos(ang)), sn = (float)(p.mscale * sin(ang));
                 const float xp = xs[partner];
                 // pair (a, b) -> (a c - b s, a s + b c)
@@ -644,6 +652,17 @@ hipError_t launch_decode_head(const DecodeHeadArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(decode_head_kernel<64>, grid, dim3(64), 0, s, a);
     else
         return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+namespace {
+__global__ void set_int_kernel(int* dst, int value) {
+    if (threadIdx.x == 0) dst[0] = value;
+}
+}  // namespace
+
+hipError_t launch_set_int(int* dst, int value, hipStream_t s) {
+    hipLaunchKernelGGL(set_int_kernel, dim3(1), dim3(64), 0, s, dst, value);
     return hipGetLastError();
 }
 

@@ -191,12 +191,19 @@ struct DecodeAttnArgs {
     int R, hq, hkv, hd;
     int n_splits, rows_per_split;
     float softcap;
+    // Non-null: the row count lives in device memory and R is read from it
+    // (a step replayed from a graph); rows per split (other row widths) are
+    // then derived in the kernel, and the combine kernel advances the count
+    // by one after every read of it has happened.
+    int* R_dev;
 };
 bool decode_group_ok(int hq, int hkv, int hd);
 constexpr int DECODE_ROWS_SPLITS = 184;   // split cap of the row-per-wave kernel
 bool decode_rows_kernel_ok(int hq, int hkv, int hd);
 void decode_split_plan(int hq, int hkv, int hd, int rows_total, int* n_splits, int* rows_per_split);
 hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s);
+// *dst = value (one thread): the device row count of a replayed decode step
+hipError_t launch_set_int(int* dst, int value, hipStream_t s);
 
 enum { GV_RESID = 0, GV_SWIGLU = 1 };
 struct GemvArgs {
@@ -220,6 +227,7 @@ struct DecodeHeadArgs {
     float eps;
     int rope_on, rope_layout, rot_dim; double theta; const float* freq; float mscale;
     int pos, hq, hkv, hd;
+    const int* pos_dev;                  // non-null: the position is read from here
     float* q; float* k_row; float* v_row;
 };
 hipError_t launch_decode_head(const DecodeHeadArgs& a, hipStream_t s);

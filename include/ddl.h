@@ -299,6 +299,36 @@ int ddl_decode_layer(ddl_ctx* ctx, ddl_mirror* m, int host_rows,
                      float* k_row, float* v_row, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* ---- the decode step as one submission --------------------------------------
+ * [P3] module doc ("Why"): the cost of a decode token is the number of
+ * submissions, one per layer at best; [P2] device_attention_layer runs the
+ * whole attention layer "in one submission".  ddl_decode_graph_create
+ * captures one ddl_decode_layer step (its seven kernels) as a HIP graph,
+ * bound to this mirror, layer and these buffers (their addresses are baked
+ * in: hidden is read, out/k_row/v_row written, at every replay).  The row
+ * count the step attends over lives in device memory (in the workspace) and
+ * the attention's split plan is sized for the mirror's capacity, so one
+ * graph serves every row count up to it.  Declines like ddl_decode_layer
+ * for the shape; returns 1 and *graph, 0, or < 0.  Nothing is enqueued.
+ *   hidden, out, k_row, v_row, workspace: as ddl_decode_layer's, device
+ *   memory that must stay in place (and workspace unshared) while the graph
+ *   exists. */
+typedef struct ddl_decode_graph ddl_decode_graph;
+int ddl_decode_graph_create(ddl_ctx* ctx, ddl_mirror* mirror, const ddl_layer* layer,
+                            const float* hidden, float* out, float* k_row,
+                            float* v_row, void* workspace, size_t workspace_bytes,
+                            ddl_decode_graph** graph);
+/* Replays the step for the token at position host_rows on `stream`: the same
+ * results, appended row and mirror bookkeeping as ddl_decode_layer with the
+ * graph's buffers.  Declines (nothing enqueued) unless the mirror's seq_len
+ * equals host_rows and its capacity is at least host_rows + 1.  When the
+ * mirror moved since the graph's last replay (an upload, an eager step) one
+ * small kernel first sets the device row count.  Returns 1, 0 or < 0 (the
+ * mirror is then marked stale). */
+int ddl_decode_graph_launch(ddl_ctx* ctx, ddl_decode_graph* graph, int host_rows,
+                            void* stream);
+void ddl_decode_graph_destroy(ddl_decode_graph* graph);
+
 /* ---- launch timing probe (a measurement aid) -------------------------------
  * Kernel classes of the two operations. */
 enum {

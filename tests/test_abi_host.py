@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_function(ddl):
     from dense_decoder_layer_amd import _native
     names = declared_functions()
-    assert len(names) == 23
+    assert len(names) == 26
     lib = _native.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ddl.h but not exported"

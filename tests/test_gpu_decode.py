@@ -361,3 +361,103 @@ def test_decode_layer_chain_and_declines(ddl):
     assert rel(dl.out.cpu().numpy(), want) <= TOL_BF16
     assert rel(dl.k_row.cpu().numpy(), wk) <= TOL_BF16
     assert ddl.ddl_mirror_seq_len(dl.mirror) == 42
+
+
+# ---------------------------------------------------------------------------
+# the decode step captured once as a HIP graph and replayed per token
+
+def test_decode_graph_replays_match_eager_steps_and_oracle(ddl):
+    cfg = dl_cfg("graph-chain", start_pos=40, gated=True, softcap=30.0, qk_norm=True,
+                 qkv_bias=True)
+    say("[decode graph] capture, 4 replays, an eager step, a rewind")
+    g_side = DecodeLayer(ddl, cfg)           # the graph's mirror
+    e_side = DecodeLayer(ddl, cfg)           # eager ddl_decode_layer on a second mirror
+    w = {n: synth.values(a) for n, a in g_side.inp.layers[0].items()}
+    f32 = dict(dtype=torch.float32, device="cuda")
+    hidden = torch.empty(cfg.d_model, **f32)
+    out, k_row, v_row = (torch.empty(n, **f32) for n in (cfg.d_model, cfg.kv_width, cfg.kv_width))
+    ws = torch.empty_like(g_side.ws)
+    graph = ddl.ddl_decode_graph_create(g_side.ctx, g_side.mirror, g_side.layer, hidden, out,
+                                        k_row, v_row, ws)
+    assert graph is not None, ddl.ddl_last_error()
+    host_k, host_v = g_side.inp.prefix_k[0].copy(), g_side.inp.prefix_v[0].copy()
+    rng = np.random.default_rng(11)
+
+    def replay_and_check(rows, x, tag):
+        hidden.copy_(torch.from_numpy(x))
+        out.fill_(7.0)
+        assert ddl.ddl_decode_graph_launch(g_side.ctx, graph, rows) == 1, ddl.ddl_last_error()
+        torch.cuda.synchronize()
+        want, wk, wv = oracle.decode_layer(x, w, cfg, host_k, host_v, rows)
+        got = out.cpu().numpy()
+        err, ek = rel(got, want), rel(k_row.cpu().numpy(), wk)
+        say(f"  {tag} rows={rows}: out rel L2 {err:.2e}  k_row {ek:.2e}")
+        assert err <= TOL_BF16 and ek <= TOL_BF16 and rel(v_row.cpu().numpy(), wv) <= TOL_BF16
+        assert ddl.ddl_mirror_seq_len(g_side.mirror) == rows + 1
+        mk, mv = g_side.mirror_row(rows)      # the appended row is the returned row
+        np.testing.assert_array_equal(mk, k_row.cpu().numpy())
+        np.testing.assert_array_equal(mv, v_row.cpu().numpy())
+        return got
+
+    for step in range(4):
+        rows = host_k.shape[0]
+        x = rng.standard_normal(cfg.d_model).astype(np.float32)
+        got = replay_and_check(rows, x, f"replay {step}")
+        # eager work between replays: the same token through ddl_decode_layer
+        assert e_side.step(rows, x) == 1
+        np.testing.assert_array_equal(e_side.k_row.cpu().numpy(), k_row.cpu().numpy())
+        assert rel(got, e_side.out.cpu().numpy()) <= TOL_BF16
+        host_k = np.vstack([host_k, k_row.cpu().numpy()])
+        host_v = np.vstack([host_v, v_row.cpu().numpy()])
+    # an eager step on the graph's own mirror, then a replay: the device row
+    # count catches up
+    rows = host_k.shape[0]
+    x = rng.standard_normal(cfg.d_model).astype(np.float32)
+    assert g_side.step(rows, x) == 1
+    host_k = np.vstack([host_k, g_side.k_row.cpu().numpy()])
+    host_v = np.vstack([host_v, g_side.v_row.cpu().numpy()])
+    replay_and_check(host_k.shape[0], rng.standard_normal(cfg.d_model).astype(np.float32),
+                     "after an eager step")
+    host_k = np.vstack([host_k, k_row.cpu().numpy()])
+    host_v = np.vstack([host_v, v_row.cpu().numpy()])
+    # a stale row count is declined with nothing touched
+    out.fill_(7.0)
+    assert ddl.ddl_decode_graph_launch(g_side.ctx, graph, 3) == 0
+    torch.cuda.synchronize()
+    assert "stale" in ddl.ddl_last_error() and bool((out == 7.0).all())
+    # the host cache rewinds to 30 rows: re-upload, replay at 30
+    host_k, host_v = host_k[:30].copy(), host_v[:30].copy()
+    assert ddl.ddl_mirror_upload(g_side.mirror, torch.from_numpy(host_k).cuda(),
+                                 torch.from_numpy(host_v).cuda(), 30) == 1
+    replay_and_check(30, rng.standard_normal(cfg.d_model).astype(np.float32), "after a rewind")
+    ddl.ddl_decode_graph_destroy(graph)
+
+
+def test_decode_graph_at_the_decode_workload(ddl):
+    # the decode workload's layer shape (32/8 heads x 128, hidden 4096, FFN
+    # 14336, gated, softcap 50) over 4096 cached rows, three replays
+    base = synth.DECODE_CONFIG
+    cfg = synth.StackConfig("dec-graph", 1, base.d_model, base.n_heads, base.n_kv_heads,
+                            base.head_dim, base.d_ff, batch=1, start_pos=4096, rope_theta=5e5,
+                            gated=True, softcap=base.softcap)
+    dl = DecodeLayer(ddl, cfg)
+    w = {n: synth.values(a) for n, a in dl.inp.layers[0].items()}
+    f32 = dict(dtype=torch.float32, device="cuda")
+    hidden = torch.empty(cfg.d_model, **f32)
+    out, k_row, v_row = (torch.empty(n, **f32) for n in (cfg.d_model, cfg.kv_width, cfg.kv_width))
+    graph = ddl.ddl_decode_graph_create(dl.ctx, dl.mirror, dl.layer, hidden, out, k_row, v_row,
+                                        dl.ws)
+    host_k, host_v = dl.inp.prefix_k[0].copy(), dl.inp.prefix_v[0].copy()
+    rng = np.random.default_rng(12)
+    for step in range(3):
+        rows = host_k.shape[0]
+        x = rng.standard_normal(cfg.d_model).astype(np.float32)
+        hidden.copy_(torch.from_numpy(x))
+        assert ddl.ddl_decode_graph_launch(dl.ctx, graph, rows) == 1, ddl.ddl_last_error()
+        torch.cuda.synchronize()
+        want, wk, _ = oracle.decode_layer(x, w, cfg, host_k, host_v, rows)
+        err = rel(out.cpu().numpy(), want)
+        say(f"[decode graph 32/8x128] rows={rows}: out rel L2 {err:.2e}")
+        assert err <= TOL_BF16 and rel(k_row.cpu().numpy(), wk) <= TOL_BF16
+        host_k = np.vstack([host_k, k_row.cpu().numpy()])
+        host_v = np.vstack([host_v, v_row.cpu().numpy()])
