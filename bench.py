@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "prefill tok/s, Llama-3.2-3B-shape 28-layer stack pp512; % bf16 MFMA peak"
 PEAK_MFMA_TFLOPS = 2516.6      # dense fp16 = bf16 MFMA, 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0
+ATTN_FORMS = {"auto": 0, "one-head": 1, "shared": 2}     # ddl.h DDL_ATTN_*
 
 
 def log(*a):
@@ -315,7 +316,7 @@ def secondary_only(which, args):
     import synth
     from dense_decoder_layer_amd.workloads import DeviceStack
     torch.cuda.set_device(0)
-    ctx = ddl.ddl_ctx_create()
+    ctx = ddl.ddl_ctx_create(attn_form=ATTN_FORMS[args.attn_form])
     stack = hidden = None
     if which == "prefix1536":
         cfg = synth.STACK_CONFIGS["llama3b_pp512"]
@@ -337,6 +338,8 @@ def main():
                     help="skip the other prefill workloads (3B over a 1536-row prefix, 8B pp4096)")
     ap.add_argument("--secondary-only", choices=("prefix1536", "pp4096"),
                     help="time one secondary workload alone (profiling aid; no headline line)")
+    ap.add_argument("--attn-form", choices=("auto", "one-head", "shared"), default="auto",
+                    help="prefill attention kernel form (measurement aid; default: the automatic choice)")
     ap.add_argument("--breakdown", action="store_true",
                     help="also time every prefill kernel class per launch (HIP events)")
     args = ap.parse_args()
@@ -358,7 +361,7 @@ def main():
     cfg = synth.STACK_CONFIGS["llama3b_pp512"]
     torch.cuda.set_device(0)
     t0 = time.time()
-    ctx = ddl.ddl_ctx_create()
+    ctx = ddl.ddl_ctx_create(attn_form=ATTN_FORMS[args.attn_form])
     layers_iter = (synth.layer_weights(cfg, l) for l in range(cfg.n_layers))
     stack = DeviceStack(ctx, cfg, layers_iter)
     bufs = stack.buffers(cfg.batch, cfg.start_pos)

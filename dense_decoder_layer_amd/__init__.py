@@ -26,6 +26,7 @@ from ._native import (DDL_K_ATTN_PREFILL, DDL_K_DECODE_ATTN, DDL_K_DECODE_HEAD, 
 from ._native import (DDL_ACT_GELU, DDL_ACT_SWIGLU, DDL_DECLINED, DDL_DTYPE_BF16,
                       DDL_DTYPE_F32, DDL_ERR_DEVICE, DDL_ERR_INJECTED, DDL_ERR_INVALID,
                       DDL_ERR_WORKSPACE, DDL_NOALLOC_SCRATCH_BYTES, DDL_ROPE_NEOX,
+                      DDL_ATTN_AUTO, DDL_ATTN_ONE_HEAD, DDL_ATTN_SHARED,
                       DDL_ROPE_NORM, CtxOpts, LayerDesc, LayerWeights)
 
 __all__ = [
@@ -94,8 +95,10 @@ class Ctx:
             ddl_ctx_destroy(self)
 
 
-def ddl_ctx_create(min_batch: int = 4, fault_after_admission: bool = False) -> Ctx:
-    opts = CtxOpts(min_batch, int(fault_after_admission))
+def ddl_ctx_create(min_batch: int = 4, fault_after_admission: bool = False,
+                   attn_form: int = 0) -> Ctx:
+    """attn_form: DDL_ATTN_AUTO, DDL_ATTN_ONE_HEAD or DDL_ATTN_SHARED."""
+    opts = CtxOpts(min_batch, int(fault_after_admission), int(attn_form))
     h = _lib().ddl_ctx_create(byref(opts))
     if not h:
         raise MemoryError("ddl_ctx_create")

@@ -15,6 +15,7 @@ DDL_ERR_WORKSPACE = -4
 DDL_ACT_SWIGLU, DDL_ACT_GELU = 0, 1
 DDL_ROPE_NEOX, DDL_ROPE_NORM = 0, 1
 DDL_DTYPE_F32, DDL_DTYPE_BF16 = 0, 1
+DDL_ATTN_AUTO, DDL_ATTN_ONE_HEAD, DDL_ATTN_SHARED = 0, 1, 2
 DDL_NOALLOC_SCRATCH_BYTES = 6 << 20
 (DDL_K_RMSNORM, DDL_K_GEMM_QKV, DDL_K_QKV_POST, DDL_K_ATTN_PREFILL, DDL_K_GEMM_WO,
  DDL_K_GEMM_GATE_UP, DDL_K_GEMM_DOWN, DDL_K_DECODE_ATTN, DDL_K_GEMV_WO, DDL_K_GEMV_GATE_UP,
@@ -22,7 +23,7 @@ DDL_NOALLOC_SCRATCH_BYTES = 6 << 20
 
 
 class CtxOpts(ctypes.Structure):
-    _fields_ = [("min_batch", c_int), ("fault_after_admission", c_int)]
+    _fields_ = [("min_batch", c_int), ("fault_after_admission", c_int), ("attn_form", c_int)]
 
 
 class LayerDesc(ctypes.Structure):

@@ -176,9 +176,12 @@ ddl_ctx* ddl_ctx_create(const ddl_ctx_opts* opts) {
     if (!c) return nullptr;
     c->min_batch = 4;
     c->fault_after_admission = 0;
+    c->attn_form = DDL_ATTN_AUTO;
     if (opts) {
         if (opts->min_batch > 0) c->min_batch = opts->min_batch;
         c->fault_after_admission = opts->fault_after_admission;
+        if (opts->attn_form == DDL_ATTN_ONE_HEAD || opts->attn_form == DDL_ATTN_SHARED)
+            c->attn_form = opts->attn_form;
     }
     return c;
 }
@@ -491,6 +494,7 @@ int ddl_prefill_dense_stack(ddl_ctx* ctx, const float* hidden, const ddl_layer* 
             a.B = batch; a.S = start_pos; a.hq = hq; a.hkv = hkv; a.hd = hd;
             a.softcap = L->softcap;
             a.window = L->window;
+            a.form = ctx->attn_form;
             ProbeScope p(ctx, DDL_K_ATTN_PREFILL, s);
             e = launch_attn_prefill(a, s);
         }

@@ -383,7 +383,9 @@ hipError_t launch_cfg(const AttnPrefillArgs& a, hipStream_t s) {
 template <int HD, bool CAP, int G>
 hipError_t launch_group(const AttnPrefillArgs& a, hipStream_t s) {
     const int packed_wgs = (a.hq / G) * ((a.B + 31) / 32);
-    if (G == 1 || packed_wgs < 512) return launch_cfg<HD, CAP, 1, 2>(a, s);
+    const bool shared = a.form == DDL_ATTN_SHARED ||
+                        (a.form != DDL_ATTN_ONE_HEAD && packed_wgs >= 512);
+    if (G == 1 || !shared) return launch_cfg<HD, CAP, 1, 2>(a, s);
     return launch_cfg<HD, CAP, G, 2>(a, s);
 }
 

@@ -349,7 +349,7 @@ bool gemm_shape_ok(int M, int N, int K, int epi) {
 //    four slices.
 //  * Anything else: 64 x 128 tiles, gate/up 128 x 128.
 namespace {
-enum Tile { T64x128, T128x128, T128x256, T64x256, T64x192 };
+enum Tile { T64x128, T128x128, T128x256, T64x256, T64x192, T128x256R };
 struct Plan {
     Tile tile;
     int splits;
@@ -377,6 +377,9 @@ Plan gemm_plan(int M, int N, int K, int epi) {
     if (epi == EPI_SWIGLU || epi == EPI_GEGLU) return {N % 256 == 0 && M > 64 ? T128x256 : T128x128, 1};
     if (epi == EPI_F32 && N % 256 == 0 && M > 64)
         return {T128x256, fill_split(((M + 127) / 128) * (N / 256), 256, nk)};
+    // large M: the gate/up tile, which fills the CUs without a K split
+    if (epi == EPI_RESID && N % 256 == 0 && ((M + 127) / 128) * (N / 256) >= 256)
+        return {T128x256R, 1};
     if (epi == EPI_RESID && N % 192 == 0 && M > 64 && ((M + 63) / 64) * (N / 192) <= 256)
         return {T64x192, fill_split(((M + 63) / 64) * (N / 192), 256, nk)};
     const int splits = split_count(((M + 63) / 64) * (N / 128), 768, nk);
@@ -412,6 +415,7 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, int splits, hipStream_t s) {
                 return (a.K / splits) % 128 == 0 ? launch_nk<64, 32, 1, 6, 3, EPI_RESID, 128>(a, splits, s)
                                                  : launch_nk<64, 32, 1, 6, 3, EPI_RESID>(a, splits, s);
             if (t == T64x256) return launch_nk<64, 32, 1, 8, 3, EPI_RESID>(a, splits, s);
+            if (t == T128x256R) return launch_nk<128, 32, 1, 8, 3, EPI_RESID>(a, splits, s);
             return launch_nk<64, 32, 1, 4, 4, EPI_RESID>(a, splits, s);
     }
     return hipErrorInvalidValue;

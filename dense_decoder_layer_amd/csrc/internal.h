@@ -14,6 +14,7 @@ typedef _Float16 f16;
 struct ddl_ctx {
     int min_batch;
     int fault_after_admission;
+    int attn_form;                      // DDL_ATTN_*
     // launch timing probe
     int probe_kind = -1, probe_max = 0, probe_count = 0;
     std::vector<hipEvent_t> probe_events;   // 2 per launch: start, end
@@ -158,6 +159,7 @@ struct AttnPrefillArgs {
     int B, S, hq, hkv, hd;
     float softcap;
     int window;                          // > 0: token at position p sees keys p-window+1 .. p
+    int form;                            // DDL_ATTN_*
 };
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s);
 

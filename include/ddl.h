@@ -67,10 +67,17 @@ typedef struct ddl_mirror ddl_mirror;
 /* Context options.  min_batch: smallest batch the prefill serves ([P1]
  * try_cuda_prefill_dense_stack declines batches under four; default 4).
  * fault_after_admission: test hook -- a call that passes admission returns
- * DDL_ERR_INJECTED before enqueueing any device work. */
+ * DDL_ERR_INJECTED before enqueueing any device work.
+ * attn_form: which prefill attention kernel form runs (a measurement and
+ * test aid; results agree to rounding): DDL_ATTN_AUTO (0, the default: one
+ * head per workgroup on small grids, a GQA group's heads sharing each K/V
+ * tile on large ones), DDL_ATTN_ONE_HEAD, DDL_ATTN_SHARED (falls back to
+ * one head when a KV head has a single query head). */
+enum { DDL_ATTN_AUTO = 0, DDL_ATTN_ONE_HEAD = 1, DDL_ATTN_SHARED = 2 };
 typedef struct {
     int min_batch;
     int fault_after_admission;
+    int attn_form;
 } ddl_ctx_opts;
 
 /* Create / destroy a context.  opts may be NULL (defaults).  Creating a

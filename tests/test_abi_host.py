@@ -44,7 +44,7 @@ def test_library_exports_every_declared_function(ddl):
 def test_struct_layouts_match_c(ddl, tmp_path):
     from dense_decoder_layer_amd import _native as N
     fields = {
-        "ddl_ctx_opts": (N.CtxOpts, ["min_batch", "fault_after_admission"]),
+        "ddl_ctx_opts": (N.CtxOpts, ["min_batch", "fault_after_admission", "attn_form"]),
         "ddl_layer_desc": (N.LayerDesc, [f for f, _ in N.LayerDesc._fields_]),
         "ddl_layer_weights": (N.LayerWeights, [f for f, _ in N.LayerWeights._fields_]),
     }

@@ -41,9 +41,9 @@ def host_values(layers):
         yield {n: synth.values(a) for n, a in w.items()}
 
 
-def gpu_run(ddl, cfg, inp, min_batch=1, hidden=None):
+def gpu_run(ddl, cfg, inp, min_batch=1, hidden=None, attn_form=0):
     from dense_decoder_layer_amd.workloads import DeviceStack
-    ctx = ddl.ddl_ctx_create(min_batch=min_batch)
+    ctx = ddl.ddl_ctx_create(min_batch=min_batch, attn_form=attn_form)
     stack = DeviceStack(ctx, cfg, inp.layers)
     bufs = stack.buffers(cfg.batch, cfg.start_pos)
     h = torch.from_numpy(inp.hidden if hidden is None else hidden).cuda()
@@ -156,6 +156,21 @@ def test_small_stacks_match_oracle(ddl, name):
         f"heads={cfg.n_heads}/{cfg.n_kv_heads}x{cfg.head_dim}")
     inp = synth.stack_inputs(cfg)
     check_parity(name, cfg, inp, gpu_run(ddl, cfg, inp), cfg.n_layers)
+
+
+# the same cases through the attention form where the query heads of a KV
+# head share each K/V tile (the automatic choice takes it only on large
+# grids); cases with one query head per KV head have no such form
+SHARED_CASES = [n for n, c in SMALL_CASES.items() if c.n_heads > c.n_kv_heads]
+
+
+@pytest.mark.parametrize("name", SHARED_CASES)
+def test_small_stacks_shared_kv_tiles_match_oracle(ddl, name):
+    cfg = SMALL_CASES[name]
+    say(f"case {name} (shared K/V tiles)")
+    inp = synth.stack_inputs(cfg)
+    check_parity(name, cfg, inp, gpu_run(ddl, cfg, inp, attn_form=ddl.DDL_ATTN_SHARED),
+                 cfg.n_layers)
 
 
 def test_deterministic_and_causal(ddl):
