@@ -385,84 +385,114 @@ __global__ __launch_bounds__(COMBINE_GROUPS * 32) void decode_attn_combine_kerne
 //          CUs).  One load covers that half of two consecutive blocks: lane
 //          l takes row 16h + l % 16, column half (l/16) % 2, block kb + l/32
 //          (two 256-byte runs per block).
+// A wave issues its loads NL at a time, all of a chunk back to back before
+// any is used, and the first chunk before x is staged (x's own loads go out
+// first: the counter completes loads in order).  Past the wave's last block a chunk repeats that
+// block (a wave-uniform clamp instead of a branch, which would make the
+// compiler wait for every load) and counts it with weight 0.
 // Lanes of a row meet by shuffles, the waves in LDS, in a fixed order.
 constexpr int GV_WAVES = 8;
-constexpr int GV_UNROLL = 4;    // fragment loads in flight per lane (8 measured no faster)
 constexpr int GV_MAXK = 15872;  // largest K the LDS stage holds (62 KB of dynamic LDS)
 
-template <int EPI, int RH>
+template <int EPI, int RH, int NL, int XV>
 __global__ __launch_bounds__(GV_WAVES * 64) void gemv_kernel(GemvArgs p) {
     static_assert(RH == 1 || (RH == 2 && EPI == GV_RESID), "row halves only for the residual form");
     extern __shared__ float xs[];   // [K]
     __shared__ float red[GV_WAVES][32];
     __shared__ float wsum[GV_WAVES];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int i = tid; i < p.K; i += GV_WAVES * 64) xs[i] = p.x[i];
+    const int nb = blockIdx.x / RH, hsel = blockIdx.x % RH;
+    const int kblocks = p.K >> 4;
+    // this wave's loads j = 0 .. nload-1: block kb0 + j * kstep (RH = 2: and
+    // the next one, for the lanes with kofs = 1; kblocks is even there)
+    const int kofs = RH == 1 ? 0 : lane >> 5;
+    const f16* wb;
+    const float* xl;
+    int kb0, kstep;
+    if constexpr (RH == 1) {
+        wb = p.W + (size_t)nb * kblocks * 512 + lane * 8;
+        xl = xs + 8 * (lane >> 5);
+        kb0 = wave;
+        kstep = GV_WAVES;
+    } else {
+        const int khalf = (lane >> 4) & 1;
+        const int fl = (lane & 15) + 16 * hsel + 32 * khalf;      // lane within the 1 KB block
+        wb = p.W + ((size_t)nb * kblocks + kofs) * 512 + fl * 8;
+        xl = xs + kofs * 16 + 8 * khalf;
+        kb0 = 2 * wave;
+        kstep = 2 * GV_WAVES;
+    }
+    const int nload = kblocks > kb0 ? (kblocks - kb0 + kstep - 1) / kstep : 0;
+    auto block_of = [&](int j) { return nload > 0 ? kb0 + min(j, nload - 1) * kstep : 0; };
+    half8 w[NL];
+    auto issue = [&](int c0) {
+#pragma unroll
+        for (int u = 0; u < NL; ++u) w[u] = *reinterpret_cast<const half8*>(wb + (size_t)block_of(c0 + u) * 512);
+        __builtin_amdgcn_sched_barrier(0);   // keep the chunk's loads together, ahead of their use
+    };
+    float acc = 0.f;
+    auto use = [&](int c0) {
+#pragma unroll
+        for (int u = 0; u < NL; ++u) {
+            const float* xv = xl + block_of(c0 + u) * 16;
+            float d = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) d += (float)w[u][jj] * xv[jj];
+            acc += (c0 + u < nload ? 1.0f : 0.0f) * d;
+        }
+    };
+
+    // x first (XV float4 a thread, clamped in range), then the weights: the
+    // counter completes loads in order, so x can be used while the weight
+    // loads are still in flight
+    const int k4 = p.K >> 2;
+    const float4* x4 = reinterpret_cast<const float4*>(p.x);
+    float4 xr[XV], gr[XV];
+#pragma unroll
+    for (int v = 0; v < XV; ++v) xr[v] = x4[min(tid + v * GV_WAVES * 64, k4 - 1)];
+    if (p.norm_g) {
+#pragma unroll
+        for (int v = 0; v < XV; ++v)
+            gr[v] = reinterpret_cast<const float4*>(p.norm_g)[min(tid + v * GV_WAVES * 64, k4 - 1)];
+    }
+    issue(0);
+    float r = 1.0f;
     if (p.norm_g) {
         float ss = 0.f;
-        for (int i = tid; i < p.K; i += GV_WAVES * 64) ss += p.x[i] * p.x[i];
+#pragma unroll
+        for (int v = 0; v < XV; ++v)
+            if (tid + v * GV_WAVES * 64 < k4)
+                ss += xr[v].x * xr[v].x + xr[v].y * xr[v].y + xr[v].z * xr[v].z + xr[v].w * xr[v].w;
         ss = wave_sum(ss);
         if (lane == 0) wsum[wave] = ss;
         __syncthreads();
         float t = 0.f;
 #pragma unroll
-        for (int w = 0; w < GV_WAVES; ++w) t += wsum[w];
-        const float r = 1.0f / sqrtf(t / (float)p.K + p.eps);
-        for (int i = tid; i < p.K; i += GV_WAVES * 64) xs[i] = xs[i] * r * p.norm_g[i];
+        for (int v = 0; v < GV_WAVES; ++v) t += wsum[v];
+        r = 1.0f / sqrtf(t / (float)p.K + p.eps);
+    }
+    float4* xs4 = reinterpret_cast<float4*>(xs);
+#pragma unroll
+    for (int v = 0; v < XV; ++v) {
+        const int i4 = tid + v * GV_WAVES * 64;
+        if (i4 < k4) {
+            float4 y = xr[v];
+            if (p.norm_g)
+                y = make_float4(y.x * r * gr[v].x, y.y * r * gr[v].y, y.z * r * gr[v].z,
+                                y.w * r * gr[v].w);
+            xs4[i4] = y;
+        }
     }
     __syncthreads();
-    const int nb = blockIdx.x / RH, hsel = blockIdx.x % RH;
-    const int kblocks = p.K >> 4;
-    float acc = 0.f;
+    use(0);
+    for (int c0 = NL; c0 < nload; c0 += NL) {
+        issue(c0);
+        use(c0);
+    }
     if constexpr (RH == 1) {
-        const f16* wb = p.W + (size_t)nb * kblocks * 512 + lane * 8;
-        const float* xl = xs + 8 * (lane >> 5);
-        int kb = wave;
-        for (; kb + (GV_UNROLL - 1) * GV_WAVES < kblocks; kb += GV_UNROLL * GV_WAVES) {
-            half8 w[GV_UNROLL];
-#pragma unroll
-            for (int u = 0; u < GV_UNROLL; ++u) w[u] = *reinterpret_cast<const half8*>(wb + (size_t)(kb + u * GV_WAVES) * 512);
-#pragma unroll
-            for (int u = 0; u < GV_UNROLL; ++u) {
-                const float* xv = xl + (kb + u * GV_WAVES) * 16;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc += (float)w[u][j] * xv[j];
-            }
-        }
-        for (; kb < kblocks; kb += GV_WAVES) {
-            const half8 w = *reinterpret_cast<const half8*>(wb + (size_t)kb * 512);
-            const float* xv = xl + kb * 16;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc += (float)w[j] * xv[j];
-        }
         acc += __shfl_xor(acc, 32, 64);
         if (lane < 32) red[wave][lane] = acc;
     } else {
-        const int khalf = (lane >> 4) & 1, kofs = lane >> 5;
-        const int fl = (lane & 15) + 16 * hsel + 32 * khalf;      // lane within the 1 KB block
-        const f16* wb = p.W + ((size_t)nb * kblocks + kofs) * 512 + fl * 8;
-        const float* xl = xs + kofs * 16 + 8 * khalf;
-        constexpr int STEP = 2 * GV_WAVES;                        // blocks per round of the waves
-        int kb = 2 * wave;                                        // this wave's pair: kb, kb + 1
-        for (; kb + (GV_UNROLL - 1) * STEP + 1 < kblocks; kb += GV_UNROLL * STEP) {
-            half8 w[GV_UNROLL];
-#pragma unroll
-            for (int u = 0; u < GV_UNROLL; ++u) w[u] = *reinterpret_cast<const half8*>(wb + (size_t)(kb + u * STEP) * 512);
-#pragma unroll
-            for (int u = 0; u < GV_UNROLL; ++u) {
-                const float* xv = xl + (kb + u * STEP) * 16;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc += (float)w[u][j] * xv[j];
-            }
-        }
-        for (; kb < kblocks; kb += STEP) {
-            if (kb + kofs < kblocks) {
-                const half8 w = *reinterpret_cast<const half8*>(wb + (size_t)kb * 512);
-                const float* xv = xl + kb * 16;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc += (float)w[j] * xv[j];
-            }
-        }
         acc += __shfl_xor(acc, 16, 64);
         acc += __shfl_xor(acc, 32, 64);
         if (lane < 16) red[wave][lane] = acc;
@@ -667,19 +697,46 @@ hipError_t launch_set_int(int* dst, int value, hipStream_t s) {
 }
 
 bool gemv_shape_ok(int K) { return K > 0 && K % 16 == 0 && K <= GV_MAXK; }
+static_assert(GV_MAXK <= 8 * 4 * GV_WAVES * 64, "x staging covers the largest K");
+
+namespace {
+// Loads a wave keeps in flight per chunk: the smallest of 8, 16, 24, 32 that
+// covers the wave's blocks, else 32 (more chunks).
+// ... and float4 of x a thread: XV * 2048 >= K.
+template <int EPI, int RH, int NL>
+hipError_t launch_gemv_xv(const GemvArgs& a, int grid, size_t lds, hipStream_t s) {
+    const dim3 block(GV_WAVES * 64);
+    const int xv = (a.K + 4 * GV_WAVES * 64 - 1) / (4 * GV_WAVES * 64);
+    if (xv <= 1) hipLaunchKernelGGL((gemv_kernel<EPI, RH, NL, 1>), dim3(grid), block, lds, s, a);
+    else if (xv <= 2) hipLaunchKernelGGL((gemv_kernel<EPI, RH, NL, 2>), dim3(grid), block, lds, s, a);
+    else if (xv <= 4) hipLaunchKernelGGL((gemv_kernel<EPI, RH, NL, 4>), dim3(grid), block, lds, s, a);
+    else hipLaunchKernelGGL((gemv_kernel<EPI, RH, NL, 8>), dim3(grid), block, lds, s, a);
+    return hipGetLastError();
+}
+
+// Loads a wave keeps in flight per chunk: 8 (4 when a wave has no more
+// blocks).  Measured at the decode shapes (hidden 4096, FFN 14336): chunks
+// of 8 took gate/up from 51.4 to 45.5 us and down from 27.9 to 25.3 us
+// against chunks of 32 -- smaller chunks leave registers for four
+// workgroups a CU, whose round trips then overlap; 4 and 6 were no better.
+template <int EPI, int RH>
+hipError_t launch_gemv_nl(const GemvArgs& a, int grid, size_t lds, hipStream_t s) {
+    const int kblocks = a.K >> 4, kstep = RH == 1 ? GV_WAVES : 2 * GV_WAVES;
+    const int nload = (kblocks + kstep - 1) / kstep;   // wave 0's, the most of any wave
+    if (nload <= 4) return launch_gemv_xv<EPI, RH, 4>(a, grid, lds, s);
+    return launch_gemv_xv<EPI, RH, 8>(a, grid, lds, s);
+}
+}  // namespace
 
 hipError_t launch_gemv(const GemvArgs& a, int epi, hipStream_t s) {
     if (!gemv_shape_ok(a.K)) return hipErrorInvalidValue;
     // GV_SWIGLU: N outputs from 2N packed rows; GV_RESID: N rows
     const int rows = epi == GV_SWIGLU ? 2 * a.N : a.N;
     if (rows % 32) return hipErrorInvalidValue;
-    const dim3 block(GV_WAVES * 64);
     const size_t lds = a.K * sizeof(float);
-    if (epi == GV_SWIGLU)
-        hipLaunchKernelGGL((gemv_kernel<GV_SWIGLU, 1>), dim3(rows / 32), block, lds, s, a);
-    else if (rows / 32 < 512)   // under two rounds of row blocks on 256 CUs: 16-row halves
-        hipLaunchKernelGGL((gemv_kernel<GV_RESID, 2>), dim3(rows / 16), block, lds, s, a);
-    else
-        hipLaunchKernelGGL((gemv_kernel<GV_RESID, 1>), dim3(rows / 32), block, lds, s, a);
-    return hipGetLastError();
+    if (epi == GV_SWIGLU) return launch_gemv_nl<GV_SWIGLU, 1>(a, rows / 32, lds, s);
+    // under two rounds of row blocks on 256 CUs: 16-row halves (their loads
+    // take block pairs, so K is a multiple of 32 there)
+    if (rows / 32 < 512 && a.K % 32 == 0) return launch_gemv_nl<GV_RESID, 2>(a, rows / 16, lds, s);
+    return launch_gemv_nl<GV_RESID, 1>(a, rows / 32, lds, s);
 }
