@@ -14,6 +14,7 @@ workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
                     [--no-decode] [--no-secondary] [--copy-calibration]
+                    [--library-gemms]
 
 --copy-calibration adds three plain 1 GiB device-to-device copies at the end,
 the reference a hardware-counter run scales FETCH_SIZE / WRITE_SIZE by.
@@ -326,6 +327,42 @@ def secondary_only(which, args):
           flush=True)
 
 
+def library_gemms(args):
+    """The four projection shapes of the 3B pp512 layer through torch's GEMMs
+    (the platform's GEMM library, fp16 in, fp16 out), the weight stored K x N
+    (torch.matmul) and N x K (torch.nn.functional.linear), each weight
+    rotated over four copies so that, as in the stack, it comes from HBM: a
+    yardstick for the GEMM kernels' rates, not part of the step."""
+    import torch
+    import torch.nn.functional as F
+    torch.cuda.set_device(0)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    shapes = {"gate_up": (512, 16384, 3072), "down": (512, 3072, 8192),
+              "qkv": (512, 5120, 3072), "wo": (512, 3072, 3072)}
+    out = {}
+    for name, (m, n, k) in shapes.items():
+        a = torch.randn(m, k, device="cuda", dtype=torch.float16, generator=g)
+        row = {"m_n_k": [m, n, k]}
+        for layout, shape, fn in (("w_kxn", (k, n), torch.matmul), ("w_nxk", (n, k), F.linear)):
+            ws = [torch.randn(*shape, device="cuda", dtype=torch.float16, generator=g) for _ in range(4)]
+            for w in ws:
+                fn(a, w)
+            torch.cuda.synchronize()
+            reps = max(args.steps, 1) * 10
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            start.record()
+            for i in range(reps):
+                fn(a, ws[i % 4])
+            end.record()
+            torch.cuda.synchronize()
+            us = start.elapsed_time(end) / reps * 1e3
+            row[layout] = {"avg_us": round(us, 2), "tflops": round(2 * m * n * k / (us * 1e-6) / 1e12, 1)}
+            del ws
+        out[name] = row
+        del a
+    print(json.dumps({"library_gemms": out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -342,6 +379,8 @@ def main():
                     help="prefill attention kernel form (measurement aid; default: the automatic choice)")
     ap.add_argument("--breakdown", action="store_true",
                     help="also time every prefill kernel class per launch (HIP events)")
+    ap.add_argument("--library-gemms", action="store_true",
+                    help="time the layer's four projection shapes through torch.matmul and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the multi-GPU sharding "
@@ -351,6 +390,9 @@ def main():
 
     if args.secondary_only:
         secondary_only(args.secondary_only, args)
+        return
+    if args.library_gemms:
+        library_gemms(args)
         return
 
     import torch
