@@ -328,7 +328,8 @@ def secondary_only(which, args):
 
 
 def library_gemms(args):
-    """The four projection shapes of the 3B pp512 layer through torch's GEMMs
+    """The four projection shapes of the 3B pp512 layer and of the 8B layer at
+    4096 tokens through torch's GEMMs
     (the platform's GEMM library, fp16 in, fp16 out), the weight stored K x N
     (torch.matmul) and N x K (torch.nn.functional.linear), each weight
     rotated over four copies so that, as in the stack, it comes from HBM: a
@@ -338,7 +339,10 @@ def library_gemms(args):
     torch.cuda.set_device(0)
     g = torch.Generator(device="cuda").manual_seed(7)
     shapes = {"gate_up": (512, 16384, 3072), "down": (512, 3072, 8192),
-              "qkv": (512, 5120, 3072), "wo": (512, 3072, 3072)}
+              "qkv": (512, 5120, 3072), "wo": (512, 3072, 3072),
+              # the 8B-shaped layer at 4096 tokens (QKV with biases: 6144 wide)
+              "8b_gate_up": (4096, 28672, 4096), "8b_down": (4096, 4096, 14336),
+              "8b_qkv": (4096, 6144, 4096), "8b_wo": (4096, 4096, 4096)}
     out = {}
     for name, (m, n, k) in shapes.items():
         a = torch.randn(m, k, device="cuda", dtype=torch.float16, generator=g)
@@ -348,7 +352,7 @@ def library_gemms(args):
             for w in ws:
                 fn(a, w)
             torch.cuda.synchronize()
-            reps = max(args.steps, 1) * 10
+            reps = max(args.steps, 1) * (10 if m <= 512 else 2)
             start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             start.record()
             for i in range(reps):
