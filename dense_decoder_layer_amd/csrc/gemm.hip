@@ -298,6 +298,143 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(GemmArgs p, int sp
     epilogue<MI, NI, EPI>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, m0 + BM <= p.M, split, rt);
 }
 
+// The 128 x 256 eight-wave tile on v_mfma_f32_16x16x32_f16, for gate/up at
+// large M (862 -> 810 us on the 8B layer at 4096 tokens against the
+// 32x32x16 form, one box; at 512 tokens the 32x32x16 form is as fast or
+// faster, and for the residual projections at 4096 tokens this form
+// measured no faster).  Wave tile 128 x 32 = 8 x 2 tiles of 16 x 16.
+// A fragment (16 rows x 32 k): lane l holds row l % 16, chunk l / 16 of
+// the 32-wide window, read from the same swizzled LDS tile as above.
+// B fragment (32 k x 16 columns): lane l holds column l % 16 and k
+// 8(l/16) .. +7 of the window, which in the 32 x 16 fragment blocks sits
+// in block 2w + (l/32), lane 16 jj + l % 16 + 32 ((l/16) % 2): one 16-byte
+// load a lane, in 256-byte runs.  Accumulator: lane l holds column l % 16
+// of rows 4(l/16) .. +3; in a gate/up tile, 16-column tile 0 is the gate
+// and tile 1 the up half of the same 16 outputs, so SwiGLU pairs them
+// within the lane.
+template <int NS, int EPI, int NK>
+__global__ __launch_bounds__(512) void gemm16_kernel(GemmArgs p) {
+    static_assert(EPI == EPI_SWIGLU || EPI == EPI_GEGLU, "gate/up epilogues only");
+    constexpr int BM = 128, BN = 256, BKT = 64, KC = 8, NT = 512, WN = 32;
+    constexpr int A_TOT = BM * KC, A_CH = A_TOT / NT, STAGE = BM * BKT * 2;
+    constexpr int MT = BM / 16, NTL = WN / 16, KW = BKT / 32;   // 16x16 tiles, k32 windows
+    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int mt = (p.M + BM - 1) / BM, nt = p.N / BN, total = mt * nt;
+    int bid = blockIdx.x;
+    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+    const int m0 = (bid % mt) * BM, n0 = (bid / mt) * BN;
+    const int nk = NK > 0 ? NK : p.K / BKT;
+
+    const f16* a_src[A_CH];
+    int a_dst[A_CH];
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+        const int idx = i * NT + tid;
+        const int r = idx / KC, c = idx % KC;
+        a_src[i] = p.A + (size_t)min(m0 + r, p.M - 1) * p.lda + c * 8;
+        a_dst[i] = r * KC + (c ^ (r & 7));
+    }
+    // B: the wave's 32 columns are fragment block (n0 + 32 wave) / 32
+    const int q = lane >> 4;
+    const f16* wbase = p.W + ((size_t)((n0 + wave * WN) / 32) * (p.K / 16) + (q >> 1)) * 512 +
+                       ((lane & 15) + 32 * (q & 1)) * 8;
+
+    half8 areg[NS][A_CH];
+    half8 breg[NS][KW][NTL];
+    auto issue = [&](int kt, auto slot_c) {
+        constexpr int slot = decltype(slot_c)::value;
+#pragma unroll
+        for (int i = 0; i < A_CH; ++i)
+            areg[slot][i] = *reinterpret_cast<const half8*>(a_src[i] + (size_t)kt * BKT);
+#pragma unroll
+        for (int w = 0; w < KW; ++w)
+#pragma unroll
+            for (int jj = 0; jj < NTL; ++jj)
+                breg[slot][w][jj] = *reinterpret_cast<const half8*>(wbase + (size_t)(kt * (BKT / 16) + 2 * w) * 512 + jj * 16 * 8);
+    };
+    auto commit = [&](auto slot_c, int buf) {
+        constexpr int slot = decltype(slot_c)::value;
+        half8* As = reinterpret_cast<half8*>(smem + buf * STAGE);
+#pragma unroll
+        for (int i = 0; i < A_CH; ++i) As[a_dst[i]] = areg[slot][i];
+    };
+
+    floatx4 acc[MT][NTL];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NTL; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    auto step = [&](int kt, auto slot_c) {
+        constexpr int slot = decltype(slot_c)::value;
+        issue(min(kt + NS - 1, nk - 1), std::integral_constant<int, (slot + NS - 1) % NS>());
+        const half8* As = reinterpret_cast<const half8*>(smem + (kt & 1) * STAGE);
+#pragma unroll
+        for (int w = 0; w < KW; ++w) {
+            half8 af[MT];
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                const int r = i * 16 + (lane & 15), c = w * 4 + q;
+                af[i] = As[r * KC + (c ^ (r & 7))];
+            }
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < NTL; ++j) acc[i][j] = mfma16x16x32(af[i], breg[slot][w][j], acc[i][j]);
+        }
+        commit(std::integral_constant<int, (slot + 1) % NS>(), (kt + 1) & 1);
+        lds_barrier();
+    };
+
+    const int col0 = n0 + wave * WN;
+    const bool full = m0 + BM <= p.M;
+    static_assert(NS == 3, "three-deep register prefetch");
+    issue(0, std::integral_constant<int, 0>());
+    issue(min(1, nk - 1), std::integral_constant<int, 1>());
+    commit(std::integral_constant<int, 0>(), 0);
+    lds_barrier();
+    if constexpr (NK > 0) {
+        static_for<NK>([&](auto kc) {
+            constexpr int kt = decltype(kc)::value;
+            step(kt, std::integral_constant<int, kt % NS>());
+        });
+    } else {
+        for (int kt = 0; kt < nk; kt += NS) {
+            step(kt, std::integral_constant<int, 0>());
+            if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>());
+            if (kt + 2 < nk) step(kt + 2, std::integral_constant<int, 2>());
+        }
+    }
+
+    const float sc = *p.inv_scale;
+    const int fcol = (col0 >> 1) + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float g = acc[i][0][e] * sc, u = acc[i][1][e] * sc;
+            const float act = EPI == EPI_GEGLU
+                                  ? 0.5f * g * (1.0f + erff(g * 0.7071067811865476f))
+                                  : g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+            const int row = m0 + i * 16 + 4 * q + e;
+            if (full || row < p.M) p.H[(size_t)row * p.ldh + fcol] = (f16)(act * u);
+        }
+}
+
+constexpr int MF16_MIN_M = 2048;   // the 16x16x32 form from here on
+
+template <int EPI>
+hipError_t launch16(const GemmArgs& a, hipStream_t s) {
+    const dim3 grid(((a.M + 127) / 128) * (a.N / 256)), block(512);
+    switch (a.K / 64) {
+        case 48: hipLaunchKernelGGL((gemm16_kernel<3, EPI, 48>), grid, block, 0, s, a); break;
+        case 64: hipLaunchKernelGGL((gemm16_kernel<3, EPI, 64>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((gemm16_kernel<3, EPI, 0>), grid, block, 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
 template <int BM, int WN, int WGM, int WGN, int NS, int EPI, int NK, int BKT>
 hipError_t launch_cfg(const GemmArgs& a, int splits, hipStream_t s) {
     const int mt = (a.M + BM - 1) / BM, nt = a.N / (WN * WGN);
@@ -400,6 +537,8 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, int splits, hipStream_t s) {
         (splits > 1 && (!a.P || epi == EPI_SWIGLU || epi == EPI_GEGLU)))
         return hipErrorInvalidValue;
     const Tile t = gemm_plan(a.M, a.N, a.K, epi).tile;
+    if (t == T128x256 && (epi == EPI_SWIGLU || epi == EPI_GEGLU) && a.M >= MF16_MIN_M)
+        return epi == EPI_SWIGLU ? launch16<EPI_SWIGLU>(a, s) : launch16<EPI_GEGLU>(a, s);
     switch (epi) {
         case EPI_SWIGLU:
             if (t == T128x256) return launch_nk<128, 32, 1, 8, 3, EPI_SWIGLU>(a, 1, s);

@@ -146,6 +146,12 @@ SMALL_CASES = {
                                              batch=130, n_layers=3),
     "post-norms-llama3b-2layers-b256": synth.STACK_CONFIGS["llama3b_pp512"].replace(
         n_layers=2, batch=256, post_norms=True),
+    # more than 2048 new tokens, a ragged count: the large-M GEMM form for
+    # the GELU FFN, and at hidden 4096 for SwiGLU and the residual
+    # projections (wo with K 4096, down with a K of no straight-line form)
+    "geglu-b2100": small("geglu-b2100", ffn_act="geglu", batch=2100),
+    "wide-b2100": small("wide-b2100", d_model=4096, n_heads=32, n_kv_heads=8, d_ff=2048,
+                        batch=2100, n_layers=1),
 }
 
 
