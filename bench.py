@@ -384,11 +384,11 @@ def main():
     ap.add_argument("--breakdown", action="store_true",
                     help="also time every prefill kernel class per launch (HIP events)")
     ap.add_argument("--library-gemms", action="store_true",
-                    help="time the layer's four projection shapes through torch's GEMMs and exit")
+                    help="time the projection shapes of the 3B and 8B layers through torch's GEMMs and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; the multi-GPU sharding "
-                                   "is a design (DESIGN.md), not a launched path",
+        print(json.dumps({"error": "this library runs on one GPU; the multi-GPU sharding "
+                                   "is a design, not a launched path",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 

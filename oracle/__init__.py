@@ -26,7 +26,7 @@ Plain float64 numpy, one step after another, in the order the pages give:
 
 The pages do not print the kernels' arithmetic, so each step is the
 textbook definition of that step of a pre-norm Llama layer; every point the
-pages leave open is a stated reading (the design doc lists them all):
+pages leave open is a stated reading:
 
 * RMSNorm is ``x / sqrt(mean(x^2) + eps) * g`` (epsilon inside the root,
   gain multiplied as is).

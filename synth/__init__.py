@@ -8,7 +8,7 @@ counter-based stream (numpy's Philox4x64-10 bit generator keyed by
 tensor can be drawn on its own, in any order, on any thread, and always
 comes out the same.
 
-Distributions (the reading stated in the design doc):
+Distributions (a stated reading: the pages fix none):
   * projection matrices and biases  ~ N(0, 0.02)
   * RMSNorm / QK-norm / post-norm gains ~ 1 + N(0, 0.02)
   * hidden rows and prefix K/V rows ~ N(0, 1), fp32
