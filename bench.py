@@ -7,10 +7,10 @@ tokens/s, the stack's fraction of dense fp16/bf16 MFMA peak, the roofline of
 the dominant kernel (the gate/up projection + SwiGLU GEMM, timed per launch
 with HIP events in a second pass of the same steps), the single-token decode
 layer at 32768 cached rows (ms per layer, decode attention as a fraction of
-HBM bandwidth), the other prefill workloads as secondary lines (the 3B stack
-over a 1536-row cached prefix, the 8B-shaped stack with biases and QK norms
-at pp4096) and the CPU oracle timed on a bounded sample of the prefill
-workload.
+HBM bandwidth and of a plain device copy's rate), the other prefill
+workloads as secondary lines (the 3B stack over a 1536-row cached prefix,
+the 8B-shaped stack with biases and QK norms at pp4096) and the CPU oracle
+timed on a bounded sample of each workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
                     [--no-decode] [--no-secondary] [--copy-calibration]
@@ -51,33 +51,42 @@ def algorithmic_flops(cfg):
     return (gemm + attn) * cfg.n_layers, 2 * cfg.batch * d * 2 * f
 
 
-def cpu_baseline(cfg, budget_s=12.0):
-    """The oracle (fp64 numpy) layer by layer over the same workload until
-    about ``budget_s`` seconds of oracle time (or the whole stack) have run;
-    drawing the inputs is not timed.  Scaled to the whole stack."""
-    import oracle
-    import synth
-    # the threads the oracle actually runs on: its matrix products use the
-    # BLAS pool (OMP_NUM_THREADS, the host's CPU share for one GPU); its
-    # elementwise steps run on one thread
+def oracle_cores():
+    """The threads the oracle actually runs on: its matrix products use the
+    BLAS pool (OMP_NUM_THREADS, the host's CPU share for one GPU); its
+    elementwise steps run on one thread."""
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
+        return int(os.environ.get("OMP_NUM_THREADS", "1"))
+
+
+def cpu_baseline(cfg, budget_s=12.0, max_layers=None):
+    """The oracle (fp64 numpy) layer by layer over the same workload (with
+    the layer's cached prefix rows when there are any) until about
+    ``budget_s`` seconds of oracle time, ``max_layers`` layers or the whole
+    stack have run; drawing the inputs is not timed.  Scaled to the whole
+    stack."""
+    import oracle
+    import synth
+    cores = oracle_cores()
     x = synth.hidden_rows(cfg)
     spent, done = 0.0, 0
-    while done < cfg.n_layers and spent < budget_s:
+    limit = cfg.n_layers if max_layers is None else min(max_layers, cfg.n_layers)
+    while done < limit and spent < budget_s:
         w = {n: synth.values(a) for n, a in synth.layer_weights(cfg, done).items()}
+        pk, pv = synth.prefix_rows(cfg, done) if cfg.start_pos > 0 else (None, None)
         t0 = time.perf_counter()
-        x, _, _ = oracle.dense_layer(x, w, cfg, cfg.start_pos)
+        x, _, _ = oracle.dense_layer(x, w, cfg, cfg.start_pos, pk, pv)
         spent += time.perf_counter() - t0
         done += 1
     per_step = spent * cfg.n_layers / done
     return {"value": round(cfg.batch / per_step, 2), "unit": "tok/s", "cores": cores,
             "host_nproc": os.cpu_count(), "kind": "oracle",
-            "sample": f"first {done} of {cfg.n_layers} layers at pp{cfg.batch} "
-                      f"(fp64 numpy oracle, {spent:.1f}s), scaled x{cfg.n_layers / done:g}"}
+            "sample": f"first {done} of {cfg.n_layers} layers at pp{cfg.batch}"
+                      + (f" over a {cfg.start_pos}-row prefix" if cfg.start_pos else "")
+                      + f" (fp64 numpy oracle, {spent:.1f}s), scaled x{cfg.n_layers / done:g}"}
 
 
 def gate_up_traffic():
@@ -218,7 +227,22 @@ def decode_bench(ddl, ctx, reps=40):
             torch.cuda.synchronize()
         sync[name] = round((time.perf_counter() - t0) / reps * 1e3, 4)
     del graphs
+    # the practical HBM roof: a plain 1 GiB device-to-device copy, bytes read
+    # plus bytes written over its time, best of 5
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    copy_ms = []
+    for _ in range(5):
+        start.record(stream)
+        dst.copy_(src)
+        end.record(stream)
+        torch.cuda.synchronize()
+        copy_ms.append(start.elapsed_time(end))
+    copy_gbs = 2 * src.nbytes / (min(copy_ms) / 1e3) / 1e9
+    del src, dst
     attn_bytes = attended * cfg.kv_width * 4 * 2 // reps     # fp32 K and V rows read per call
+    # the tail's fp16 weights: wo, gate and up, down
+    tail_bytes = 2 * (cfg.d_model * cfg.n_heads * cfg.head_dim + 3 * cfg.d_model * cfg.d_ff)
     return {"config": f"{cfg.name}: {cfg.rows} cached rows, {cfg.n_heads} q / {cfg.n_kv_heads} "
                       f"KV heads x {cfg.head_dim}, softcap {cfg.softcap:g}, sigmoid gate, "
                       f"wo + RMSNorm + SwiGLU {cfg.d_ff} tail, hidden {cfg.d_model}",
@@ -230,7 +254,29 @@ def decode_bench(ddl, ctx, reps=40):
             "attn_bytes": attn_bytes,
             "attn_hbm_gbs": round(attn_bytes / (attn_ms / 1e3) / 1e9, 1),
             "attn_hbm_frac": round(attn_bytes / (attn_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+            "copy_gbs": round(copy_gbs, 1),                # a plain device copy on the same box
+            "attn_frac_of_copy": round(attn_bytes / (attn_ms / 1e3) / 1e9 / copy_gbs, 4),
+            # ddl_attn_layer's HBM bytes (K/V rows + tail weights) over its time
+            "layer_hbm_gbs": round((attn_bytes + tail_bytes) / (layer_ms / 1e3) / 1e9, 1),
             "tail": tail}
+
+
+def cpu_baseline_decode(reps=3):
+    """The oracle's attention layer (fp64 numpy) at the decode workload, 32768
+    cached rows, one token per call; drawing and converting the inputs is not
+    timed."""
+    import oracle
+    import synth
+    cfg = synth.DECODE_CONFIG
+    inp = synth.decode_inputs(cfg)
+    w = {n: synth.values(a) for n, a in inp["weights"].items()}
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.attn_layer(inp["q"], inp["k"], inp["v"], inp["gate"], inp["cache_k"],
+                          inp["cache_v"], cfg.rows, w, cfg, inp["residual"])
+    per = (time.perf_counter() - t0) / reps
+    return {"ms_per_layer": round(per * 1e3, 2), "cores": oracle_cores(), "kind": "oracle",
+            "sample": f"{reps} tokens at {cfg.rows} cached rows (fp64 numpy oracle)"}
 
 
 def timed_steps(step, steps):
@@ -488,6 +534,15 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample ...")
         result["cpu_baseline"] = cpu_baseline(cfg)
+        # the same oracle beside the other workloads: the 3B stack over its
+        # prefix (bounded like the headline's), the 8B stack on two layers
+        # (extrapolated to 32), and one decode token
+        for line, name, kw in zip(result.get("secondary", []),
+                                  ("llama3b_prefix1536", "llama8b_pp4096_extras"),
+                                  (dict(budget_s=8.0), dict(max_layers=2))):
+            line["cpu_oracle"] = cpu_baseline(synth.STACK_CONFIGS[name], **kw)
+        if "decode" in result:
+            result["decode"]["cpu_oracle"] = cpu_baseline_decode()
     print(json.dumps(result), flush=True)
 
 
