@@ -198,3 +198,24 @@ def test_build_works_in_a_checkout_without_the_library(tmp_path):
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
     assert (tmp_path / "dense_decoder_layer_amd" / "libddl.so").exists()
+
+
+def test_empty_and_short_batches_decline_before_touching_anything(ddl):
+    """A call with no new tokens (or fewer than the context's min_batch) is
+    declined before any pointer is read: the pointers here are host
+    sentinels that a device access would fault on, and the layer pointer
+    is never dereferenced."""
+    from dense_decoder_layer_amd import _native as N
+    lib = N.lib()
+    ctx = ddl.ddl_ctx_create(min_batch=4)
+    sentinel = ctypes.c_void_p(0x1000)
+    layers = (ctypes.c_void_p * 1)(0x2000)
+    rows_arr = (ctypes.c_void_p * 1)(0x3000)
+    prefix_rows = (ctypes.c_int * 1)(0)
+    for batch in (0, 3):
+        rc = lib.ddl_prefill_dense_stack(ctx.handle, sentinel, layers, 1, batch, 0, None, None,
+                                         prefix_rows, sentinel, rows_arr, rows_arr, sentinel,
+                                         0, None)
+        assert rc == ddl.DDL_DECLINED, (batch, rc)
+        assert b"min_batch" in lib.ddl_last_error()
+    ddl.ddl_ctx_destroy(ctx)
