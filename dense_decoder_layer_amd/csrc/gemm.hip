@@ -476,10 +476,15 @@ bool gemm_shape_ok(int M, int N, int K, int epi) {
 //  * stacked QKV: the same tile, K split so the grid comes closest to 256
 //    workgroups (80 tiles at 512 tokens: three slices, 240 workgroups; 23 us
 //    against 28 us with two).
+//    From 2048 rows the gate/up tile is issued as 16x16x32 MFMAs
+//    (gemm16_kernel below).
 //  * wo and down, width a multiple of 192: 64 x 192 tiles of six waves,
 //    split to fill 256 workgroups (two slices at 512 tokens).  For down this
 //    matches the four-way split of 64 x 128 tiles in time with one partial
 //    sum instead of three for the next norm to add.
+//  * wo and down at large M, once 128 x 256 tiles alone fill the CUs (4096
+//    tokens): the gate/up tile with the residual epilogue, unsplit (8B
+//    layer: down 641 -> 504 us, wo 193 -> 161 us against 64 x 256 tiles).
 //  * other residual shapes: 64 x 128 tiles (four waves, three workgroups fit
 //    a CU) split until 768 workgroup slots fill, each slice keeping at least
 //    24 k-tiles; 64 x 256 tiles of eight waves where that gives fewer than
