@@ -15,7 +15,8 @@
 // through LDS in a fixed order at the end.
 //
 // Keys and values were staged once per layer as fp16: K16 [kv head][key][hd]
-// and Vt16 [kv head][hd][key].  Each key split owns a two-stage LDS ring.
+// and Vt16 [kv head][hd][key], the keys of each 16-key group ordered so that
+// a lane's V^T operand is one 16-byte LDS read.  Each key split owns a two-stage LDS ring.
 // With one head per workgroup a wave runs through its own tiles with no
 // barrier, the next tile's DMA (global_load_lds_dwordx4) in flight while one
 // is used.  With G heads the split's G waves share each tile's DMA, and the
@@ -279,9 +280,8 @@ __global__ __launch_bounds__(G * NKS * 64) void attn_prefill_kernel(AttnPrefillA
             const int sw = (r >> 1) & 3;
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
-                const half4 lo = *reinterpret_cast<const half4*>(vrow + (((2 * kh) ^ sw) * 8) + 4 * g2);
-                const half4 hi = *reinterpret_cast<const half4*>(vrow + (((2 * kh + 1) ^ sw) * 8) + 4 * g2);
-                const half8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                // the staged key order puts this lane's 8 keys in chunk 2kh + g2
+                const half8 vf = *reinterpret_cast<const half8*>(vrow + (((2 * kh + g2) ^ sw) * 8));
                 o[hb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[kh], o[hb], 0, 0, 0);
             }
         }

@@ -126,7 +126,13 @@ hipError_t launch_rope_table(float2* tab, int batch, int start_pos, int rot_dim,
 // Staged fp16 K/V of one layer for the attention kernel, tcap rows per KV
 // head (a multiple of 32, at least S + 32*(ceil(B/32)+1)):
 //   k16  [hkv][tcap][hd]   key j = cached row j (j < S) or new row j - S
-//   vt16 [hkv][hd][tcap]   the same values transposed
+//   vt16 [hkv][hd][tcap]   the same values transposed, key j at position
+//                          vt_pos(j): within each aligned group of 16 keys,
+//                          keys 8..11 and 4..7 trade places, so that the 8
+//                          keys one lane of the attention's V^T operand needs
+//                          (4g..4g+3 and 8+4g..8+4g+3, g = 0 or 1) are the
+//                          16 contiguous bytes at position 8g
+__host__ __device__ inline int vt_pos(int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); }
 struct QkvPostArgs {
     const float* part; int nparts;       // split-K partials of qkv, [nparts][B][nqkv]
     float* qkv; int nqkv;               // [B][nqkv] GEMM output (a gated layer's

@@ -280,26 +280,28 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs p) {
         vt[e + 3][tl] = (f16)x[i].w;
     }
     __syncthreads();
-    // row e of Vt16 gets this block's 32 keys: 16-byte stores of 8 keys when
-    // the block's first key is 8-aligned, else one key at a time
-    if ((p.S & 7) == 0) {
+    // row e of Vt16 gets this block's 32 keys at their positions vt_pos(key):
+    // when the block's first key is 16-aligned its keys fill its own 32
+    // positions, written as 16-byte stores of 8 positions; else one key at a
+    // time (a 16-key group then spans two writers, each writing its keys)
+    if ((p.S & 15) == 0) {
         for (int idx = tid; idx < HD * 4; idx += 256) {
             const int e = idx >> 2, t0 = (idx & 3) * 8;
             half8 w;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) w[u] = vt[e][t0 + u];
+            for (int u = 0; u < 8; ++u) w[u] = vt[e][vt_pos(t0 + u)];
             *reinterpret_cast<half8*>(p.vt16 + ((size_t)g * HD + e) * p.tcap + p.S + blk * 32 + t0) = w;
         }
     } else {
         for (int idx = tid; idx < HD * 32; idx += 256) {
             const int e = idx >> 5, t = idx & 31;
-            p.vt16[((size_t)g * HD + e) * p.tcap + p.S + blk * 32 + t] = vt[e][t];
+            p.vt16[((size_t)g * HD + e) * p.tcap + vt_pos(p.S + blk * 32 + t)] = vt[e][t];
         }
     }
 }
 
 // Cached rows [0, S) of one layer into the staged fp16 layouts: K16[g][j]
-// and Vt16[g][e][j].  One block per (32 rows, KV head).
+// and Vt16[g][e][vt_pos(j)].  One block per (32 rows, KV head).
 template <int HD>
 __global__ __launch_bounds__(256) void stage_prefix_kernel(StagePrefixArgs p) {
     __shared__ f16 vt[HD][33];
@@ -323,7 +325,7 @@ __global__ __launch_bounds__(256) void stage_prefix_kernel(StagePrefixArgs p) {
     __syncthreads();
     for (int idx = tid; idx < HD * 32; idx += 256) {
         const int e = idx >> 5, t = idx & 31, j = blk * 32 + t;
-        if (j < p.S) p.vt16[((size_t)g * HD + e) * p.tcap + j] = vt[e][t];
+        if (j < p.S) p.vt16[((size_t)g * HD + e) * p.tcap + vt_pos(j)] = vt[e][t];
     }
 }
 
