@@ -137,21 +137,24 @@ __global__ __launch_bounds__(G * NKS * 64) void attn_prefill_kernel(AttnPrefillA
     // NDMA (the last ones repeat instruction j when NDMA is not a multiple of
     // G: the same bytes to the same place).  K instruction d covers rows
     // RPI*d .. RPI*d + RPI-1 (RPI = 64/KCH rows: 4 at HD=128, 8 at HD=64);
-    // lane l takes row RPI*d + l/KCH and chunk (l % KCH) ^ (row % 8), which
-    // keeps the K rows XOR-swizzled.  V^T instruction v = d - K_INSTR covers
-    // hd rows 16v .. 16v+15, four 16-byte chunks (8 keys) each; chunk c of
-    // row r sits at c ^ ((r/2) % 4).  Both offsets are a per-lane part plus
-    // a multiple of d: the K swizzle depends on d only through d % 2 (RPI=4)
-    // or not at all (RPI=8), and (r/2) % 4 = (l/8) % 4 for every v.
+    // lane l takes row RPI*d + l/KCH and chunk (l % KCH) ^ (row % KCH), so
+    // the 16 rows one pass of a fragment read touches sit in 16 (HD=128) or
+    // 8 (HD=64) different chunk positions.  V^T instruction v = d - K_INSTR
+    // covers hd rows 16v .. 16v+15, four 16-byte chunks (8 keys) each; chunk
+    // c of row r sits at c ^ ((r/4) % 4), so the four rows of a pass that
+    // share banks (r, r+4, r+8, r+12) read four different positions.  Both
+    // offsets are a per-lane part plus a part of d: the K swizzle of row
+    // RPI*d + l/KCH is (l % KCH) ^ (l/KCH) ^ (RPI*d % KCH), and (r/4) % 4 =
+    // (l/16) % 4 for every v.
     constexpr int RPI = 64 / KCH;
     const f16* kbase = p.k16 + (size_t)g * p.tcap * HD;
     const f16* vbase = p.vt16 + (size_t)g * HD * p.tcap;
-    auto k_lane = [&](int par) {
-        const int row = par * RPI + lane / KCH;
-        return row * HD + (((lane % KCH) ^ (row & 7)) * 8);
+    const int kswz = (lane % KCH) ^ (lane / KCH);
+    const int krow = (lane / KCH) * HD;
+    auto k_ofs = [&](int d) {   // d wave-uniform
+        return (size_t)d * RPI * HD + krow + ((kswz ^ ((RPI * d) & (KCH - 1))) * 8);
     };
-    const int kofs0 = k_lane(0), kofs1 = k_lane(1);
-    const int vofs = (lane >> 2) * p.tcap + (((lane & 3) ^ ((lane >> 3) & 3)) * 8);
+    const int vofs = (lane >> 2) * p.tcap + (((lane & 3) ^ ((lane >> 4) & 3)) * 8);
     const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
     auto issue = [&](int tile, int slot) {
         const size_t k0 = (size_t)tile * KT;
@@ -160,7 +163,7 @@ __global__ __launch_bounds__(G * NKS * 64) void attn_prefill_kernel(AttnPrefillA
             const int d0 = j + r * G;
             const int d = d0 < NDMA ? d0 : j;     // wave-uniform
             const f16* src = d < K_INSTR
-                ? kbase + k0 * HD + (size_t)(d & ~1) * RPI * HD + ((d & 1) ? kofs1 : kofs0)
+                ? kbase + k0 * HD + k_ofs(d)
                 : vbase + k0 + (size_t)(d - K_INSTR) * 16 * p.tcap + vofs;
             dma16(src, ring_lds + slot * STAGE + d * 1024);
         }
@@ -221,7 +224,7 @@ __global__ __launch_bounds__(G * NKS * 64) void attn_prefill_kernel(AttnPrefillA
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int cc = ks * 2 + g2;
-            st[ks % CH] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ks[ql * KCH + (cc ^ (ql & 7))], qf[ks],
+            st[ks % CH] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ks[ql * KCH + (cc ^ (ql & (KCH - 1)))], qf[ks],
                                                                  st[ks % CH], 0, 0, 0);
         }
         // lane holds key k0 + 8*(e/4) + 4*g2 + e%4 of query qrow.  Without a
@@ -277,7 +280,7 @@ __global__ __launch_bounds__(G * NKS * 64) void attn_prefill_kernel(AttnPrefillA
         for (int hb = 0; hb < HB; ++hb) {
             const int r = hb * 32 + ql;
             const f16* vrow = Vs + r * KT;
-            const int sw = (r >> 1) & 3;
+            const int sw = (r >> 2) & 3;
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
                 // the staged key order puts this lane's 8 keys in chunk 2kh + g2
